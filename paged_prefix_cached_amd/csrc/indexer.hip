@@ -1,0 +1,155 @@
+// Indexer scores: I[i,t] = scale_t * sum_h w[i,h] * max(0, <q[i,h,:], e4m3(k_t)>) for
+// t <= pos(i), else -inf.
+//
+// Sources: vLLM AgentX article (news.ainew.jp), "DeepSeek V4" (the indexer has 64 heads
+// but yields one global top-k per token); GLM-5.3 report (aisoku.org), "What's new" (the
+// indexer picks 2,048 tokens; its cost is quadratic in the prompt).  The per-token key
+// scale is positive, so it commutes with the ReLU and is applied once after the head sum.
+//
+// A workgroup of 8 waves owns 8 query rows (one per wave) and a chunk of keys.  Key
+// tiles of 64 tokens are gathered through the block table, upcast exactly from FP8 to
+// bf16 and staged in LDS once for all 8 queries.  Each wave keeps its query's 64 x 128
+// bf16 heads in registers (A operand) and computes C[heads x keys] with
+// v_mfma_f32_16x16x32_bf16: in the C layout a lane holds 4 heads of one key, so the
+// weighted ReLU head sum is 16 fused multiply-adds in registers plus a 2-step reduction
+// across the 4 lane groups.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kD = 128, kBs = 64;
+constexpr int kWaves = 8;
+constexpr int kKT = 64;                  // keys per LDS tile
+constexpr int kChunk = 8192;             // keys per workgroup
+constexpr int kKStride = kD + 8;         // bf16 per key row in LDS (272 B)
+
+__device__ __forceinline__ int find_seq(const int32_t* q_start, int num_seqs, int i) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {                      // last s with q_start[s] <= i
+    const int mid = (lo + hi + 1) >> 1;
+    if (q_start[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int NHT>   // head tiles of 16 (num_heads / 16)
+__global__ __launch_bounds__(512) void indexer_kernel(IndexerArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t k_s[kKT * kKStride];
+  __shared__ float sc_s[kKT];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m16 = lane & 15, grp = lane >> 4;
+  const int n_chunks = (a.max_total_len + kChunk - 1) / kChunk;
+  const int qblk = blockIdx.x / n_chunks, chunk = blockIdx.x % n_chunks;
+  const int i0 = qblk * kWaves;
+  const int s = find_seq(a.q_start, a.num_seqs, i0);
+  // every row of the block must belong to sequence s: rows of another sequence are
+  // handled by a second pass over the same block (rare: only at sequence boundaries)
+  const int c0 = chunk * kChunk;
+  for (int seq = s; seq < a.num_seqs; ++seq) {
+    const int qs = a.q_start[seq];
+    const int nl = min(a.new_len[seq], a.max_new_len);
+    if (qs > i0 + kWaves - 1) break;
+    const int cached = a.cached_len[seq];
+    const int total = min(cached + nl, a.max_total_len);
+    const int n_lblocks = (total + kBs - 1) / kBs;
+    const int32_t* bt_row = a.bt + (size_t)seq * a.bt_stride;
+    const int i = i0 + wave;
+    const bool mine = i < a.n_q && i >= qs && i < qs + nl;
+    const int pos = mine ? min(cached + (i - qs), total - 1) : -1;
+    // highest position of the block's rows in this sequence
+    const int i_last = min(i0 + kWaves, min(qs + nl, a.n_q)) - 1;
+    const int blk_max_pos = min(cached + (i_last - qs), total - 1);
+    const int c1 = min(c0 + kChunk, a.max_total_len);
+    if (mine && chunk == 0) a.valid_len[i] = pos + 1;
+    // ---- Q in registers: A operand [16 heads x 32 dims] per (head tile, k-step)
+    u32x4 qa[NHT][4];
+    float wv[NHT][4];
+    if (mine) {
+      const uint16_t* qp = a.q_idx + (size_t)i * (NHT * 16) * kD;
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qa[ht][ks] = ld16(qp + (size_t)(16 * ht + m16) * kD + 32 * ks + 8 * grp);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wv[ht][r] = a.w[(size_t)i * (NHT * 16) + 16 * ht + 4 * grp + r];
+      }
+    } else {
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qa[ht][ks] = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wv[ht][r] = 0.f;
+      }
+    }
+    float* srow = mine ? a.scores + (size_t)i * a.score_stride : nullptr;
+    const int kc_end = min(c1, blk_max_pos + 1);
+    for (int kb = c0; kb < kc_end; kb += kKT) {
+      __syncthreads();
+      // gather + upcast 64 keys: 64 x 128 B = 512 chunks of 16 B, one per thread
+      {
+        const int key = tid >> 3, dc = tid & 7;
+        const int t = kb + key;
+        const int pb = t < total ? phys_block(bt_row, t / kBs, n_lblocks, a.num_blocks) : -1;
+        u32x4 raw = pb >= 0 ? ld16(a.keys + ((size_t)pb * kBs + t % kBs) * kD + 16 * dc) : u32x4{0, 0, 0, 0};
+        uint32_t bf[8];
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+          const u32x2 c = fp8x4_to_bf16x4(raw[w4]);
+          bf[2 * w4] = c.x;
+          bf[2 * w4 + 1] = c.y;
+        }
+        uint16_t* kp = k_s + key * kKStride + 16 * dc;
+        st16(kp, u32x4{bf[0], bf[1], bf[2], bf[3]});
+        st16(kp + 8, u32x4{bf[4], bf[5], bf[6], bf[7]});
+        if (dc == 0) sc_s[key] = pb >= 0 ? a.key_scale[(size_t)pb * kBs + t % kBs] : 0.f;
+      }
+      __syncthreads();
+      if (!mine || kb > pos) continue;
+#pragma unroll
+      for (int st = 0; st < kKT / 16; ++st) {
+        u32x4 kb4[4];
+        const uint16_t* kp = k_s + (16 * st + m16) * kKStride + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kb4[ks] = *reinterpret_cast<const u32x4*>(kp + 32 * ks);
+        float part = 0.f;
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) {
+          f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) c = mfma16x16x32(qa[ht][ks], kb4[ks], c);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) part = fmaf(wv[ht][r], fmaxf(c[r], 0.f), part);
+        }
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        const int t = kb + 16 * st + m16;
+        if (grp == 0 && t <= pos && t < c1) srow[t] = part * sc_s[16 * st + m16] + 0.f;
+      }
+    }
+    // keys of this chunk past the row's position: -inf (the tile loop wrote t <= pos)
+    if (mine) {
+      for (int t = max(c0, pos + 1) + lane; t < c1; t += 64) srow[t] = -INFINITY;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_indexer_scores(const IndexerArgs& a, hipStream_t stream) {
+  const int n_chunks = (a.max_total_len + kChunk - 1) / kChunk;
+  const unsigned grid = (unsigned)((a.n_q + kWaves - 1) / kWaves) * n_chunks;
+  if (grid == 0) return hipSuccess;
+  switch (a.num_heads / 16) {
+    case 1: hipLaunchKernelGGL(indexer_kernel<1>, dim3(grid), dim3(512), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(indexer_kernel<2>, dim3(grid), dim3(512), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(indexer_kernel<3>, dim3(grid), dim3(512), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(indexer_kernel<4>, dim3(grid), dim3(512), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,447 @@
+// C ABI of the paged-attention library: argument validation, workspace layout, launch.
+// Every check happens before anything is enqueued; on error nothing is launched.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local char g_detail[512];
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+bool is_gqa_pool(const pa_kv_pool* p) { return p->kv_dtype == PA_BF16; }
+
+pa_status check_gqa_pool(const pa_kv_pool* p) {
+  if (p == nullptr) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+  if (p->kv_dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "GQA pool must be PA_BF16");
+  if (p->block_size != 16) return fail(PA_ERR_UNSUPPORTED, "GQA pool block_size must be 16 (got %d)", p->block_size);
+  if (p->head_dim_qk != p->head_dim_v || (p->head_dim_qk != 64 && p->head_dim_qk != 128))
+    return fail(PA_ERR_UNSUPPORTED, "GQA head_dim must be 64 or 128 with head_dim_qk == head_dim_v");
+  if (p->num_kv_heads < 1 || p->num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_kv_heads and num_blocks must be >= 1");
+  if (p->k == nullptr || p->v == nullptr) return fail(PA_ERR_INVALID_ARG, "pool k/v is NULL");
+  if (!aligned(p->k, 16) || !aligned(p->v, 16)) return fail(PA_ERR_INVALID_ARG, "pool k/v must be 16-byte aligned");
+  return PA_OK;
+}
+
+pa_status check_fp8_pool(const pa_kv_pool* p, int d_qk, int d_v, const char* what) {
+  if (p == nullptr) return fail(PA_ERR_INVALID_ARG, "%s pool is NULL", what);
+  if (p->kv_dtype != PA_FP8_E4M3) return fail(PA_ERR_UNSUPPORTED, "%s pool must be PA_FP8_E4M3", what);
+  if (p->block_size != 64) return fail(PA_ERR_UNSUPPORTED, "%s pool block_size must be 64 (got %d)", what, p->block_size);
+  if (p->num_kv_heads != 1) return fail(PA_ERR_UNSUPPORTED, "%s pool must have num_kv_heads == 1", what);
+  if (p->head_dim_qk != d_qk || p->head_dim_v != d_v)
+    return fail(PA_ERR_UNSUPPORTED, "%s pool head dims must be %d/%d (got %d/%d)", what, d_qk, d_v,
+                p->head_dim_qk, p->head_dim_v);
+  if (p->num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  if (p->k == nullptr || p->scale == nullptr) return fail(PA_ERR_INVALID_ARG, "%s pool k/scale is NULL", what);
+  if (!aligned(p->k, 16) || !aligned(p->scale, 4)) return fail(PA_ERR_INVALID_ARG, "%s pool must be 16-byte aligned", what);
+  return PA_OK;
+}
+
+pa_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return PA_OK;
+}
+
+#define PA_TRY(x)                       \
+  do {                                  \
+    const pa_status st_ = (x);          \
+    if (st_ != PA_OK) return st_;       \
+  } while (0)
+
+// ---- decode workspace layout: partial outputs then partial log2-sum-exp
+struct DecodeLayout {
+  int max_splits, rows, d_v, split;
+  size_t o_bytes, lse_bytes;
+  size_t total() const { return o_bytes + lse_bytes; }
+};
+
+DecodeLayout decode_layout(int num_seqs, int q_per_seq, int num_q_heads, int max_context_len, bool mla) {
+  DecodeLayout l;
+  l.split = mla ? pa::kDecodeSplitMla : pa::kDecodeSplitGqa;
+  l.max_splits = max_context_len > 0 ? ceil_div(max_context_len, l.split) : 0;
+  l.rows = q_per_seq * num_q_heads;
+  l.d_v = 0;
+  l.o_bytes = 0;
+  l.lse_bytes = 0;
+  return l;
+}
+
+void finish_layout(DecodeLayout& l, int num_seqs, int d_v) {
+  l.d_v = d_v;
+  l.o_bytes = round_up((size_t)num_seqs * l.max_splits * l.rows * d_v * sizeof(float), 256);
+  l.lse_bytes = round_up((size_t)num_seqs * l.max_splits * l.rows * sizeof(float), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    default: return "PA_ERR_UNKNOWN";
+  }
+}
+
+const char* pa_last_error_detail(void) { return g_detail; }
+
+int32_t pa_version(void) { return 1; }
+
+// ------------------------------------------------------------------------- prefill
+size_t paged_attn_prefill_workspace_size(int32_t, int32_t, int32_t, int32_t, const pa_kv_pool*) {
+  return 0;
+}
+
+pa_status paged_attn_prefill(const void* q, const pa_kv_pool* pool, const int32_t* block_table,
+                             int32_t bt_stride, const int32_t* cached_len, const int32_t* new_len,
+                             const int32_t* q_start, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t max_new_len, int32_t max_total_len, float scale, void* out,
+                             float* lse, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  g_detail[0] = 0;
+  PA_TRY(check_gqa_pool(pool));
+  if (q == nullptr || out == nullptr || block_table == nullptr || cached_len == nullptr ||
+      new_len == nullptr || q_start == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(PA_ERR_INVALID_ARG, "q/out must be 16-byte aligned");
+  if (num_seqs < 0 || max_new_len < 0 || max_total_len < 0 || bt_stride < 1)
+    return fail(PA_ERR_INVALID_ARG, "negative size or bt_stride < 1");
+  if (num_q_heads < 1 || num_q_heads % pool->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+  const int G = num_q_heads / pool->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(PA_ERR_UNSUPPORTED, "group size %d not in {1,2,4,8}", G);
+  if ((long)bt_stride * pool->block_size < max_total_len)
+    return fail(PA_ERR_INVALID_ARG, "bt_stride * block_size < max_total_len");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (num_seqs == 0 || max_new_len == 0) return PA_OK;
+  pa::GqaPrefillArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(pool->k);
+  a.v = static_cast<const uint16_t*>(pool->v);
+  a.bt = block_table;
+  a.cached_len = cached_len;
+  a.new_len = new_len;
+  a.q_start = q_start;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.bt_stride = bt_stride;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim_qk;
+  a.num_blocks = pool->num_blocks;
+  a.max_new_len = max_new_len;
+  a.max_total_len = max_total_len;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  (void)hipGetLastError();
+  return launched(pa::launch_gqa_prefill(a, stream), "prefill launch");
+}
+
+// ------------------------------------------------------------------------- decode
+static pa_status check_decode(const pa_kv_pool* pool, int32_t num_seqs, int32_t q_per_seq,
+                              int32_t num_q_heads, int32_t max_context_len, int32_t bt_stride) {
+  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+  if (num_seqs < 0 || max_context_len < 0 || bt_stride < 1)
+    return fail(PA_ERR_INVALID_ARG, "negative size or bt_stride < 1");
+  if (q_per_seq < 1 || q_per_seq > 4) return fail(PA_ERR_UNSUPPORTED, "q_per_seq must be 1..4");
+  if (is_gqa_pool(pool)) {
+    PA_TRY(check_gqa_pool(pool));
+    if (num_q_heads < 1 || num_q_heads % pool->num_kv_heads != 0)
+      return fail(PA_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+    const int G = num_q_heads / pool->num_kv_heads;
+    if (G > 16 || q_per_seq * G > 16)
+      return fail(PA_ERR_UNSUPPORTED, "q_per_seq * group size must be <= 16 (got %d)", q_per_seq * G);
+  } else {
+    PA_TRY(check_fp8_pool(pool, 576, 512, "MLA"));
+    if (num_q_heads < 1 || num_q_heads > 128 || num_q_heads % 16 != 0)
+      return fail(PA_ERR_UNSUPPORTED, "MLA num_q_heads must be a multiple of 16 up to 128");
+  }
+  if ((long)bt_stride * pool->block_size < max_context_len)
+    return fail(PA_ERR_INVALID_ARG, "bt_stride * block_size < max_context_len");
+  return PA_OK;
+}
+
+size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t q_per_seq, int32_t num_q_heads,
+                                        int32_t max_context_len, const pa_kv_pool* pool) {
+  if (pool == nullptr || num_seqs < 0 || q_per_seq < 1 || num_q_heads < 1 || max_context_len < 0) return 0;
+  const bool mla = !is_gqa_pool(pool);
+  DecodeLayout l = decode_layout(num_seqs, q_per_seq, num_q_heads, max_context_len, mla);
+  finish_layout(l, num_seqs, pool->head_dim_v);
+  return l.total();
+}
+
+pa_status paged_attn_decode(const void* q, const pa_kv_pool* pool, const int32_t* block_table,
+                            int32_t bt_stride, const int32_t* context_len, int32_t num_seqs,
+                            int32_t q_per_seq, int32_t num_q_heads, int32_t max_context_len,
+                            float scale, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  g_detail[0] = 0;
+  PA_TRY(check_decode(pool, num_seqs, q_per_seq, num_q_heads, max_context_len, bt_stride));
+  if (q == nullptr || out == nullptr || block_table == nullptr || context_len == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(PA_ERR_INVALID_ARG, "q/out must be 16-byte aligned");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  const bool mla = !is_gqa_pool(pool);
+  DecodeLayout l = decode_layout(num_seqs, q_per_seq, num_q_heads, max_context_len, mla);
+  finish_layout(l, num_seqs, pool->head_dim_v);
+  if (num_seqs == 0 || max_context_len == 0) return PA_OK;
+  if (workspace == nullptr || workspace_bytes < l.total())
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", l.total(), workspace_bytes);
+  if (!aligned(workspace, 16)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + l.o_bytes);
+  (void)hipGetLastError();
+  if (!mla) {
+    pa::GqaDecodeArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(pool->k);
+    a.v = static_cast<const uint16_t*>(pool->v);
+    a.bt = block_table;
+    a.context_len = context_len;
+    a.part_o = part_o;
+    a.part_lse = part_lse;
+    a.bt_stride = bt_stride;
+    a.num_seqs = num_seqs;
+    a.q_per_seq = q_per_seq;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = pool->num_kv_heads;
+    a.head_dim = pool->head_dim_qk;
+    a.num_blocks = pool->num_blocks;
+    a.max_context_len = max_context_len;
+    a.max_splits = l.max_splits;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    PA_TRY(launched(pa::launch_gqa_decode(a, stream), "decode launch"));
+  } else {
+    pa::MlaDecodeArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.kv = static_cast<const uint8_t*>(pool->k);
+    a.kv_scale = pool->scale;
+    a.bt = block_table;
+    a.context_len = context_len;
+    a.part_o = part_o;
+    a.part_lse = part_lse;
+    a.bt_stride = bt_stride;
+    a.num_seqs = num_seqs;
+    a.q_per_seq = q_per_seq;
+    a.num_q_heads = num_q_heads;
+    a.num_blocks = pool->num_blocks;
+    a.max_context_len = max_context_len;
+    a.max_splits = l.max_splits;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    PA_TRY(launched(pa::launch_mla_decode(a, stream), "MLA decode launch"));
+  }
+  pa::CombineArgs c{};
+  c.part_o = part_o;
+  c.part_lse = part_lse;
+  c.context_len = context_len;
+  c.out = static_cast<uint16_t*>(out);
+  c.lse = lse;
+  c.num_seqs = num_seqs;
+  c.rows = l.rows;
+  c.head_dim = pool->head_dim_v;
+  c.max_splits = l.max_splits;
+  c.split = l.split;
+  c.max_context_len = max_context_len;
+  return launched(pa::launch_combine(c, stream), "combine launch");
+}
+
+// ------------------------------------------------------------------------- indexer + top-k
+static size_t idx_scores_bytes(int32_t n_q, int32_t max_total_len) {
+  return round_up((size_t)n_q * max_total_len * sizeof(float), 256);
+}
+
+size_t mla_indexer_topk_workspace_size(int32_t n_q, int32_t num_idx_heads, int32_t max_total_len,
+                                       int32_t k) {
+  (void)num_idx_heads;
+  (void)k;
+  if (n_q < 0 || max_total_len < 0) return 0;
+  return idx_scores_bytes(n_q, max_total_len) + round_up((size_t)n_q * sizeof(int32_t), 256);
+}
+
+pa_status mla_indexer_topk(const void* q_idx, const float* w, const pa_kv_pool* idx_pool,
+                           const int32_t* block_table, int32_t bt_stride,
+                           const int32_t* cached_len, const int32_t* new_len,
+                           const int32_t* q_start, int32_t num_seqs, int32_t n_q,
+                           int32_t num_idx_heads, int32_t max_new_len, int32_t max_total_len,
+                           int32_t k, int32_t* topk_idx, float* scores_out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  g_detail[0] = 0;
+  PA_TRY(check_fp8_pool(idx_pool, 128, 0, "indexer"));
+  if (q_idx == nullptr || w == nullptr || block_table == nullptr || cached_len == nullptr ||
+      new_len == nullptr || q_start == nullptr || topk_idx == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(q_idx, 16) || !aligned(w, 4) || (scores_out && !aligned(scores_out, 4)))
+    return fail(PA_ERR_INVALID_ARG, "misaligned pointer");
+  if (num_seqs < 0 || n_q < 0 || max_new_len < 0 || max_total_len < 0 || bt_stride < 1)
+    return fail(PA_ERR_INVALID_ARG, "negative size or bt_stride < 1");
+  if (num_idx_heads < 16 || num_idx_heads > 64 || num_idx_heads % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "num_idx_heads must be 16, 32, 48 or 64");
+  if (k < 1 || k > 4096) return fail(PA_ERR_UNSUPPORTED, "k must be 1..4096");
+  if ((long)bt_stride * idx_pool->block_size < max_total_len)
+    return fail(PA_ERR_INVALID_ARG, "bt_stride * block_size < max_total_len");
+  const size_t need = mla_indexer_topk_workspace_size(n_q, num_idx_heads, max_total_len, k);
+  if (n_q == 0 || num_seqs == 0) return PA_OK;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (!aligned(workspace, 16)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  float* scores = scores_out ? scores_out : static_cast<float*>(workspace);
+  int32_t* valid = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + idx_scores_bytes(n_q, max_total_len));
+  (void)hipGetLastError();
+  pa::IndexerArgs a{};
+  a.q_idx = static_cast<const uint16_t*>(q_idx);
+  a.w = w;
+  a.keys = static_cast<const uint8_t*>(idx_pool->k);
+  a.key_scale = idx_pool->scale;
+  a.bt = block_table;
+  a.cached_len = cached_len;
+  a.new_len = new_len;
+  a.q_start = q_start;
+  a.scores = scores;
+  a.valid_len = valid;
+  a.bt_stride = bt_stride;
+  a.num_seqs = num_seqs;
+  a.n_q = n_q;
+  a.num_heads = num_idx_heads;
+  a.num_blocks = idx_pool->num_blocks;
+  a.max_new_len = max_new_len;
+  a.max_total_len = max_total_len;
+  a.score_stride = max_total_len;
+  PA_TRY(launched(pa::launch_indexer_scores(a, stream), "indexer launch"));
+  pa::TopkArgs t{};
+  t.scores = scores;
+  t.valid_len = valid;
+  t.out = topk_idx;
+  t.n_rows = n_q;
+  t.row_stride = max_total_len;
+  t.k = k;
+  t.max_valid = max_total_len;
+  return launched(pa::launch_topk(t, stream), "top-k launch");
+}
+
+// ------------------------------------------------------------------------- sparse MLA
+size_t sparse_mla_attn_workspace_size(int32_t, int32_t, int32_t) { return 0; }
+
+pa_status sparse_mla_attn(const void* q, const pa_kv_pool* pool, const int32_t* block_table,
+                          int32_t bt_stride, const int32_t* q_seq, const int32_t* topk_idx,
+                          int32_t n_q, int32_t k, int32_t num_q_heads, float scale, void* out,
+                          float* lse, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  g_detail[0] = 0;
+  PA_TRY(check_fp8_pool(pool, 576, 512, "MLA"));
+  if (q == nullptr || out == nullptr || block_table == nullptr || q_seq == nullptr || topk_idx == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(PA_ERR_INVALID_ARG, "q/out must be 16-byte aligned");
+  if (n_q < 0 || bt_stride < 1) return fail(PA_ERR_INVALID_ARG, "negative size or bt_stride < 1");
+  if (k < 1 || k > 8192) return fail(PA_ERR_UNSUPPORTED, "k must be 1..8192");
+  if (num_q_heads < 16 || num_q_heads > 128 || num_q_heads % 16 != 0 || (num_q_heads > 64 && num_q_heads % 64 != 0))
+    return fail(PA_ERR_UNSUPPORTED, "num_q_heads must be 16..64 in steps of 16, or 128");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (n_q == 0) return PA_OK;
+  (void)hipGetLastError();
+  pa::SparseMlaArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint8_t*>(pool->k);
+  a.kv_scale = pool->scale;
+  a.bt = block_table;
+  a.q_seq = q_seq;
+  a.topk = topk_idx;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.bt_stride = bt_stride;
+  a.n_q = n_q;
+  a.k = k;
+  a.num_q_heads = num_q_heads;
+  a.num_blocks = pool->num_blocks;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return launched(pa::launch_sparse_mla(a, stream), "sparse MLA launch");
+}
+
+// ------------------------------------------------------------------------- test hooks
+pa_status pa_test_gather_kv(const pa_kv_pool* pool, const int32_t* block_table, int32_t bt_stride,
+                            int32_t seq, int32_t n_tokens, void* k_out, void* v_out,
+                            float* scale_out, hipStream_t stream) {
+  g_detail[0] = 0;
+  if (pool == nullptr || block_table == nullptr || k_out == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  const bool fp8 = pool->kv_dtype == PA_FP8_E4M3;
+  if (fp8) {
+    if (pool->k == nullptr || pool->scale == nullptr || scale_out == nullptr || pool->num_kv_heads != 1 ||
+        pool->head_dim_qk % 16 != 0 || pool->block_size < 1)
+      return fail(PA_ERR_INVALID_ARG, "bad FP8 pool for gather");
+  } else {
+    PA_TRY(check_gqa_pool(pool));
+    if (v_out == nullptr) return fail(PA_ERR_INVALID_ARG, "v_out is NULL");
+  }
+  if (seq < 0 || n_tokens < 0 || bt_stride < 1 || (long)bt_stride * pool->block_size < n_tokens)
+    return fail(PA_ERR_INVALID_ARG, "bad seq / n_tokens / bt_stride");
+  if (!aligned(k_out, 16) || (v_out && !aligned(v_out, 16))) return fail(PA_ERR_INVALID_ARG, "outputs must be 16-byte aligned");
+  (void)hipGetLastError();
+  pa::GatherArgs a{};
+  a.k = pool->k;
+  a.v = pool->v;
+  a.scale = pool->scale;
+  a.bt_row = block_table + (size_t)seq * bt_stride;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.scale_out = scale_out;
+  a.n_tokens = n_tokens;
+  a.num_blocks = pool->num_blocks;
+  a.block_size = pool->block_size;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.row_bytes = fp8 ? pool->head_dim_qk : pool->head_dim_qk * 2;
+  a.is_fp8 = fp8 ? 1 : 0;
+  return launched(pa::launch_gather(a, stream), "gather launch");
+}
+
+size_t pa_test_topk_workspace_size(int32_t, int32_t) { return 0; }
+
+pa_status pa_test_topk_from_scores(const float* scores, const int32_t* valid_len, int32_t n_rows,
+                                   int32_t row_stride, int32_t k, int32_t* out_idx, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  g_detail[0] = 0;
+  if (scores == nullptr || valid_len == nullptr || out_idx == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (n_rows < 0 || row_stride < 0) return fail(PA_ERR_INVALID_ARG, "negative size");
+  if (k < 1 || k > 4096) return fail(PA_ERR_UNSUPPORTED, "k must be 1..4096");
+  (void)hipGetLastError();
+  pa::TopkArgs t{};
+  t.scores = scores;
+  t.valid_len = valid_len;
+  t.out = out_idx;
+  t.n_rows = n_rows;
+  t.row_stride = row_stride;
+  t.k = k;
+  t.max_valid = row_stride;
+  return launched(pa::launch_topk(t, stream), "top-k launch");
+}
+
+}  // extern "C"

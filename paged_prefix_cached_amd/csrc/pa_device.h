@@ -1,0 +1,92 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, MFMA wrappers, format
+// conversions and the block-table walk.
+//
+// MFMA lane layouts used throughout (64-lane wavefront):
+//   v_mfma_f32_16x16x32_bf16:  A[16 x 32]: lane l holds row l%16, k = 8*(l/16) .. +7
+//                              B[32 x 16]: lane l holds col l%16, k = 8*(l/16) .. +7
+//                              C[16 x 16]: lane l holds col l%16, rows 4*(l/16) + i, i<4
+//   v_mfma_f32_32x32x16_bf16:  A[32 x 16]: lane l holds row l%32, k = 8*(l/32) .. +7
+//                              B[16 x 32]: lane l holds col l%32, k = 8*(l/32) .. +7
+//                              C[32 x 32]: lane l holds col l%32,
+//                                          rows 8*(i/4) + 4*(l/32) + i%4, i<16
+// The reduction index k may be relabelled freely as long as A and B agree, which the
+// kernels use to feed softmax probabilities straight from a C tile into the next MFMA.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Two floats -> packed bf16x2 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Four OCP E4M3FN bytes -> four bf16 (exact: every E4M3 value is a bf16 value).  The
+// hardware converter gives fp32; the bf16 is its upper half.
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t src) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)src, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)src, true);
+  u32x2 r;
+  r.x = __builtin_amdgcn_perm(__float_as_uint(lo.y), __float_as_uint(lo.x), 0x07060302u);
+  r.y = __builtin_amdgcn_perm(__float_as_uint(hi.y), __float_as_uint(hi.x), 0x07060302u);
+  return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Unaligned-free 16-byte global load / store helpers.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Physical block of logical block `lb` of a sequence, or -1 when lb is past the
+// sequence's blocks or the table entry is out of range (the caller then uses zeros).
+__device__ __forceinline__ int32_t phys_block(const int32_t* __restrict__ bt_row, int32_t lb,
+                                              int32_t n_lblocks, int32_t num_blocks) {
+  if (lb >= n_lblocks) return -1;
+  int32_t b = bt_row[lb];
+  return (b >= 0 && b < num_blocks) ? b : -1;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).  This
+// maps the hardware id so that consecutive logical ids run on the same XCD, which keeps
+// workgroups that read the same KV range together in one L2.
+__device__ __forceinline__ int32_t xcd_swizzle(int32_t hw_id, int32_t n) {
+  const int32_t n8 = n & ~7;
+  if (hw_id >= n8) return hw_id;
+  return (hw_id & 7) * (n8 >> 3) + (hw_id >> 3);
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int lanes) {
+  for (int o = lanes >> 1; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_xor(float v, int lanes) {
+  for (int o = lanes >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+}  // namespace pa

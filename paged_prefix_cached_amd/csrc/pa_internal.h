@@ -1,0 +1,119 @@
+// Host-side launch interfaces between the C ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Keys per split of the decode key range.  Each split yields a partial (o, lse) pair
+// that the combine kernel merges in split order.
+constexpr int kDecodeSplitGqa = 1024;
+constexpr int kDecodeSplitMla = 8192;
+
+struct GqaPrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* bt;
+  const int32_t* cached_len;
+  const int32_t* new_len;
+  const int32_t* q_start;
+  uint16_t* out;
+  float* lse;
+  int32_t bt_stride, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks;
+  int32_t max_new_len, max_total_len;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+struct GqaDecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* bt;
+  const int32_t* context_len;
+  float* part_o;      // [S][max_splits][T*Hq][D]
+  float* part_lse;    // [S][max_splits][T*Hq], log2 units
+  int32_t bt_stride, num_seqs, q_per_seq, num_q_heads, num_kv_heads, head_dim, num_blocks;
+  int32_t max_context_len, max_splits;
+  float scale_log2;
+};
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* context_len;   // [S]
+  uint16_t* out;                // [S][rows][D]
+  float* lse;                   // [S][rows] or null
+  int32_t num_seqs, rows, head_dim, max_splits, split, max_context_len;
+};
+
+struct MlaDecodeArgs {
+  const uint16_t* q;            // [S][T][Hq][576]
+  const uint8_t* kv;            // [NB][64][576]
+  const float* kv_scale;        // [NB][64]
+  const int32_t* bt;
+  const int32_t* context_len;
+  float* part_o;                // [S][max_splits][T*Hq][512]
+  float* part_lse;
+  int32_t bt_stride, num_seqs, q_per_seq, num_q_heads, num_blocks, max_context_len, max_splits;
+  float scale_log2;
+};
+
+struct SparseMlaArgs {
+  const uint16_t* q;            // [n_q][Hq][576]
+  const uint8_t* kv;
+  const float* kv_scale;
+  const int32_t* bt;
+  const int32_t* q_seq;
+  const int32_t* topk;          // [n_q][k]
+  uint16_t* out;                // [n_q][Hq][512]
+  float* lse;
+  int32_t bt_stride, n_q, k, num_q_heads, num_blocks;
+  float scale_log2;
+};
+
+struct IndexerArgs {
+  const uint16_t* q_idx;        // [n_q][H][128]
+  const float* w;               // [n_q][H]
+  const uint8_t* keys;          // [NB][64][128]
+  const float* key_scale;       // [NB][64]
+  const int32_t* bt;
+  const int32_t* cached_len;
+  const int32_t* new_len;
+  const int32_t* q_start;
+  float* scores;                // [n_q][score_stride]
+  int32_t* valid_len;           // [n_q] written: pos(i)+1 (0 for rows outside any sequence)
+  int32_t bt_stride, num_seqs, n_q, num_heads, num_blocks, max_new_len, max_total_len;
+  int32_t score_stride;
+};
+
+struct TopkArgs {
+  const float* scores;          // [n_rows][row_stride]
+  const int32_t* valid_len;     // [n_rows]
+  int32_t* out;                 // [n_rows][k]
+  int32_t n_rows, row_stride, k, max_valid;
+};
+
+struct GatherArgs {
+  const void* k;
+  const void* v;
+  const float* scale;
+  const int32_t* bt_row;
+  void* k_out;
+  void* v_out;
+  float* scale_out;
+  int32_t n_tokens, num_blocks, block_size, num_kv_heads, row_bytes;  // row_bytes: one token of one head
+  int32_t is_fp8;
+};
+
+hipError_t launch_gqa_prefill(const GqaPrefillArgs& a, hipStream_t s);
+hipError_t launch_gqa_decode(const GqaDecodeArgs& a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_mla_decode(const MlaDecodeArgs& a, hipStream_t s);
+hipError_t launch_sparse_mla(const SparseMlaArgs& a, hipStream_t s);
+hipError_t launch_indexer_scores(const IndexerArgs& a, hipStream_t s);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+
+}  // namespace pa

@@ -1,0 +1,29 @@
+"""Shared helpers of the GPU parity tests: tolerances and error metrics."""
+import numpy as np
+
+import oracle
+
+# bf16 outputs vs the fp64 oracle: max |err| <= 1e-2 and L1 ratio sum|err|/sum|ref| <= 2e-3.
+# FP8 paths (the oracle dequantises the same bytes): max |err| <= 3e-2, and the same L1
+# ratio bound is also enforced.
+BF16_MAX_ABS, BF16_L1 = 1e-2, 2e-3
+FP8_MAX_ABS, FP8_L1 = 3e-2, 2e-3
+LSE_ABS = 2e-3
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    d = np.abs(got.astype(np.float64) - ref)
+    return float(d.max()), float(d.sum() / max(np.abs(ref).sum(), 1e-300))
+
+
+def assert_close(got, ref, max_abs, l1, what=""):
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    mx, r = errors(got, ref)
+    print(f"{what}: max_abs={mx:.3e} l1_ratio={r:.3e}", flush=True)
+    assert mx <= max_abs and r <= l1, f"{what}: max_abs={mx:.3e} (<= {max_abs}) l1={r:.3e} (<= {l1})"
+
+
+def bf16_out(t) -> np.ndarray:
+    """Device bf16 tensor -> float64 host array (exact)."""
+    import torch
+    return oracle.bf16_to_f64(t.detach().view(torch.int16).cpu().numpy().view(np.uint16))

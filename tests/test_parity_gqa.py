@@ -1,0 +1,140 @@
+"""GPU parity: paged GQA/MHA prefill and decode against the fp64 oracle.
+
+Inputs are seeded synthetic workloads (workloads.gen); every expected value is computed
+by oracle/ on the CPU from the same bytes.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from workloads.device import GqaOnDevice
+from gpu_util import BF16_L1, BF16_MAX_ABS, LSE_ABS, assert_close, bf16_out
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill(pa, dev, lse=True):
+    import torch
+    wl = dev.wl
+    lse_t = torch.empty((wl.q.shape[0], wl.num_q_heads), dtype=torch.float32, device="cuda") if lse else None
+    out = pa.paged_attn_prefill(dev.q, dev.pool, dev.bt, dev.cached, dev.n_new, dev.q_start,
+                                num_q_heads=wl.num_q_heads, max_new_len=dev.max_new,
+                                max_total_len=dev.max_total, scale=wl.scale, lse=lse_t)
+    torch.cuda.synchronize()
+    return out, lse_t
+
+
+def test_gather_bit_exact(pa_lib):
+    import torch
+    wl = W.make_gqa(21, lengths=[256, 37, 1], n_new=[16, 5, 1], num_q_heads=8, num_kv_heads=8, head_dim=64)
+    dev = GqaOnDevice(wl)
+    for s in range(wl.num_seqs):
+        L = int(wl.total_len[s])
+        k = torch.empty((L, 8, 64), dtype=torch.bfloat16, device="cuda")
+        v = torch.empty_like(k)
+        pa_lib.pa_test_gather_kv(dev.pool, dev.bt, s, L, k, v)
+        torch.cuda.synchronize()
+        kc, vc = wl.kv_contiguous(s)
+        assert np.array_equal(k.view(torch.int16).cpu().numpy().view(np.uint16), kc)
+        assert np.array_equal(v.view(torch.int16).cpu().numpy().view(np.uint16), vc)
+
+
+def test_prefill_tiny_config(pa_lib):
+    """1 sequence, MHA 8 x 64, 240 cached tokens in 15 shuffled blocks + 16 new tokens."""
+    wl = W.make_prefill_tiny(1)
+    dev = GqaOnDevice(wl)
+    out, lse = _prefill(pa_lib, dev)
+    ref_o, ref_l = oracle.paged_gqa_attention(wl, 0)
+    assert_close(bf16_out(out), ref_o, BF16_MAX_ABS, BF16_L1, "prefill tiny")
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_l, atol=LSE_ABS)
+
+
+@pytest.mark.parametrize("G,D", [(1, 64), (2, 128), (4, 128), (8, 64), (4, 64)])
+def test_prefill_ragged(pa_lib, G, D):
+    cached = [0, 5, 1000, 33, 300]
+    new = [1, 17, 130, 300, 64]
+    lengths = [c + n for c, n in zip(cached, new)]
+    Hkv = 2
+    wl = W.make_gqa(30 + G + D, lengths=lengths, n_new=new, num_q_heads=Hkv * G, num_kv_heads=Hkv,
+                    head_dim=D)
+    dev = GqaOnDevice(wl)
+    out, lse = _prefill(pa_lib, dev)
+    got = bf16_out(out)
+    lg = lse.cpu().numpy()
+    for s in range(wl.num_seqs):
+        ro, rl = oracle.paged_gqa_attention(wl, s)
+        a, b = wl.q_start[s], wl.q_start[s + 1]
+        assert_close(got[a:b], ro, BF16_MAX_ABS, BF16_L1, f"prefill G={G} D={D} seq={s}")
+        np.testing.assert_allclose(lg[a:b], rl, atol=LSE_ABS)
+
+
+def test_prefill_peaked_softmax(pa_lib):
+    """Stress: queries x8 make the softmax peaked (tolerances bind harder)."""
+    wl = W.make_gqa(41, lengths=[700, 129], n_new=[200, 129], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                    q_mult=8.0)
+    dev = GqaOnDevice(wl)
+    out, _ = _prefill(pa_lib, dev, lse=False)
+    got = bf16_out(out)
+    for s in range(2):
+        ro, _ = oracle.paged_gqa_attention(wl, s)
+        assert_close(got[wl.q_start[s]:wl.q_start[s + 1]], ro, BF16_MAX_ABS, BF16_L1, f"peaked seq={s}")
+
+
+def _decode(pa, dev, T, lse=True):
+    import torch
+    wl = dev.wl
+    S = wl.num_seqs
+    q = dev.q.view(S, T, wl.num_q_heads, wl.head_dim)
+    lse_t = torch.empty((S, T, wl.num_q_heads), dtype=torch.float32, device="cuda") if lse else None
+    out = pa.paged_attn_decode(q, dev.pool, dev.bt, dev.total_len, q_per_seq=T, num_q_heads=wl.num_q_heads,
+                               max_context_len=dev.max_total, scale=wl.scale, lse=lse_t)
+    torch.cuda.synchronize()
+    return out, lse_t
+
+
+@pytest.mark.parametrize("T,G,D,shuffle", [(1, 4, 128, False), (1, 4, 128, True), (4, 4, 128, False),
+                                            (2, 8, 64, False), (1, 1, 64, False), (3, 2, 128, True)])
+def test_decode_sessions(pa_lib, T, G, D, shuffle):
+    """Decode with sessions sharing 90% of their blocks; lengths span 1..several splits."""
+    wl = W.make_gqa_decode(50 + T * 10 + G, n_sessions=3, members=3, lo=20, hi=5000, q_per_seq=T,
+                           num_q_heads=2 * G, num_kv_heads=2, head_dim=D, shuffle_batch=shuffle,
+                           keep_content=True)
+    dev = GqaOnDevice(wl)
+    out, lse = _decode(pa_lib, dev, T)
+    got = bf16_out(out).reshape(wl.num_seqs * T, wl.num_q_heads, D)
+    lg = lse.cpu().numpy().reshape(wl.num_seqs * T, wl.num_q_heads)
+    for s in range(wl.num_seqs):
+        ro, rl = oracle.paged_gqa_attention(wl, s)
+        assert_close(got[s * T:(s + 1) * T], ro, BF16_MAX_ABS, BF16_L1, f"decode T={T} G={G} seq={s}")
+        np.testing.assert_allclose(lg[s * T:(s + 1) * T], rl, atol=LSE_ABS)
+
+
+def test_decode_edge_lengths_and_determinism(pa_lib):
+    """Contexts of 1, 16, 17, 1023, 1024, 1025 and 4097 tokens; two runs bit-identical."""
+    import torch
+    lengths = [1, 16, 17, 1023, 1024, 1025, 4097]
+    wl = W.make_gqa(61, lengths=lengths, n_new=[1] * 7, num_q_heads=32, num_kv_heads=8, head_dim=128)
+    dev = GqaOnDevice(wl)
+    out1, _ = _decode(pa_lib, dev, 1)
+    out2, _ = _decode(pa_lib, dev, 1)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    got = bf16_out(out1).reshape(7, 32, 128)
+    for s in range(7):
+        ro, _ = oracle.paged_gqa_attention(wl, s)
+        assert_close(got[s:s + 1], ro, BF16_MAX_ABS, BF16_L1, f"decode L={lengths[s]}")
+
+
+def test_decode_full_size_sampled(pa_lib):
+    """The benchmarked decode workload at full size (64 sequences, 8 sessions, contexts
+    4K-142K); a sample of sequences is checked against the oracle."""
+    wl = W.make_gqa_decode(2)
+    dev = GqaOnDevice(wl)
+    out, lse = _decode(pa_lib, dev, 1)
+    got = bf16_out(out).reshape(64, 32, 128)
+    lg = lse.cpu().numpy().reshape(64, 32)
+    order = np.argsort(wl.total_len)
+    for s in [int(order[0]), int(order[31]), int(order[-1]), 9]:
+        ro, rl = oracle.paged_gqa_attention(wl, s)
+        assert_close(got[s:s + 1], ro, BF16_MAX_ABS, BF16_L1, f"decode full seq={s} L={wl.total_len[s]}")
+        np.testing.assert_allclose(lg[s:s + 1], rl, atol=LSE_ABS)

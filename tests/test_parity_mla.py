@@ -1,0 +1,187 @@
+"""GPU parity: FP8-latent MLA decode (MTP), indexer scores + top-k, sparse MLA.
+
+The oracle dequantises the same FP8 bytes the kernels read.  Top-k index sets are
+compared bit-exactly against the oracle's top-k run on the GPU's own scores (identical
+scores); against the oracle's fp64 scores only near-ties at the k-th score may differ.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from workloads.device import MlaOnDevice
+from gpu_util import FP8_L1, FP8_MAX_ABS, LSE_ABS, assert_close, bf16_out
+
+pytestmark = pytest.mark.gpu
+
+
+def _mla_decode(pa, dev, T):
+    import torch
+    mla = dev.mla
+    S = mla.num_seqs
+    q = dev.q.view(S, T, mla.num_q_heads, 576)
+    lse = torch.empty((S, T, mla.num_q_heads), dtype=torch.float32, device="cuda")
+    out = pa.paged_attn_decode(q, dev.pool, dev.bt, dev.total_len, q_per_seq=T, num_q_heads=mla.num_q_heads,
+                               max_context_len=dev.max_total, scale=mla.scale, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _mla_ref(mla, s):
+    L = int(mla.total_len[s])
+    codes = oracle.gather_paged(mla.kv_pool, mla.block_table[s], L)
+    sc = oracle.gather_paged(mla.kv_scale[..., None], mla.block_table[s], L)[:, 0]
+    return oracle.mla_attention(mla.q_rows(s), codes, sc, mla.q_pos(s), mla.scale), codes, sc
+
+
+def test_gather_fp8_bit_exact(pa_lib):
+    import torch
+    mla = W.make_mla_decode(71, lengths=[130, 64, 5], num_q_heads=16, keep_content=True)
+    dev = MlaOnDevice(mla)
+    for s in range(3):
+        L = int(mla.total_len[s])
+        k = torch.empty((L, 576), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((L,), dtype=torch.float32, device="cuda")
+        pa_lib.pa_test_gather_kv(dev.pool, dev.bt, s, L, k, None, sc)
+        torch.cuda.synchronize()
+        c, cs = mla.kv_contiguous(s)
+        assert np.array_equal(k.cpu().numpy(), c) and np.array_equal(sc.cpu().numpy(), cs)
+
+
+@pytest.mark.parametrize("T,Hq", [(4, 64), (1, 64), (4, 16), (2, 32)])
+def test_mla_decode(pa_lib, T, Hq):
+    lengths = [T, 63, 64, 65, 3000, 8192 + 100, 17000]
+    mla = W.make_mla_decode(72 + T, lengths=lengths, q_per_seq=T, num_q_heads=Hq)
+    dev = MlaOnDevice(mla)
+    out, lse = _mla_decode(pa_lib, dev, T)
+    got = bf16_out(out).reshape(len(lengths) * T, Hq, 512)
+    lg = lse.cpu().numpy().reshape(len(lengths) * T, Hq)
+    for s in range(len(lengths)):
+        (ro, rl), _, _ = _mla_ref(mla, s)
+        assert_close(got[s * T:(s + 1) * T], ro, FP8_MAX_ABS, FP8_L1, f"mla T={T} Hq={Hq} L={lengths[s]}")
+        np.testing.assert_allclose(lg[s * T:(s + 1) * T], rl, atol=LSE_ABS)
+
+
+def test_mla_decode_peaked(pa_lib):
+    mla = W.make_mla_decode(79, lengths=[5000, 20000], q_per_seq=4, num_q_heads=64, q_mult=8.0)
+    dev = MlaOnDevice(mla)
+    out, _ = _mla_decode(pa_lib, dev, 4)
+    got = bf16_out(out).reshape(8, 64, 512)
+    for s in range(2):
+        (ro, _), _, _ = _mla_ref(mla, s)
+        assert_close(got[s * 4:(s + 1) * 4], ro, FP8_MAX_ABS, FP8_L1, f"mla peaked s={s}")
+
+
+def test_topk_hook_ties_and_short_rows(pa_lib):
+    import torch
+    scores = W.tie_scores(3, 12, 5000)
+    valid = np.array([5000, 4999, 2048, 2047, 100, 1, 4096, 3000, 2049, 5000, 777, 4500], np.int32)
+    scores[1, 7] = -0.0
+    scores[1, 9] = 0.0
+    st = torch.from_numpy(scores).cuda()
+    vt = torch.from_numpy(valid).cuda()
+    for k in (2048, 1, 100):
+        got = pa_lib.pa_test_topk_from_scores(st, vt, k).cpu().numpy()
+        for r in range(12):
+            ref = oracle.topk_indices(scores[r].astype(np.float64), valid[r], k)
+            assert np.array_equal(got[r], ref), (k, r)
+
+
+def test_topk_hook_random_scores(pa_lib):
+    import torch
+    rng = np.random.default_rng(5)
+    scores = rng.standard_normal((16, 20000)).astype(np.float32)
+    scores[3, :5000] = scores[3, 0]          # a long run of equal values
+    valid = rng.integers(1, 20001, 16).astype(np.int32)
+    valid[:4] = 20000
+    got = pa_lib.pa_test_topk_from_scores(torch.from_numpy(scores).cuda(), torch.from_numpy(valid).cuda(),
+                                          2048).cpu().numpy()
+    for r in range(16):
+        assert np.array_equal(got[r], oracle.topk_indices(scores[r].astype(np.float64), valid[r], 2048)), r
+
+
+def _indexer(pa, dev, k):
+    import torch
+    n_q = dev.q_idx.shape[0]
+    scores = torch.empty((n_q, dev.max_total), dtype=torch.float32, device="cuda")
+    topk = pa.mla_indexer_topk(dev.q_idx, dev.w, dev.idx_pool, dev.bt, dev.cached, dev.n_new, dev.q_start,
+                               max_new_len=dev.max_new, max_total_len=dev.max_total, k=k, scores_out=scores)
+    torch.cuda.synchronize()
+    return topk, scores
+
+
+def _idx_keys(mla, idx, s):
+    L = int(mla.total_len[s])
+    kc = oracle.gather_paged(idx.idx_pool, mla.block_table[s], L)
+    ks = oracle.gather_paged(idx.idx_scale[..., None], mla.block_table[s], L)[:, 0]
+    return kc, ks
+
+
+@pytest.mark.parametrize("H", [64, 32])
+def test_indexer_topk(pa_lib, H):
+    lengths, n_new = [300 + 37, 5000 + 100, 70], [37, 100, 70]
+    mla, idx = W.make_sparse_mla(81, lengths=lengths, n_new=n_new, num_q_heads=64, idx_heads=H)
+    dev = MlaOnDevice(mla, idx)
+    k = 256
+    topk, scores = _indexer(pa_lib, dev, k)
+    topk = topk.cpu().numpy()
+    sc = scores.cpu().numpy().astype(np.float64)
+    for s in range(3):
+        kc, ks = _idx_keys(mla, idx, s)
+        a, b = mla.q_start[s], mla.q_start[s + 1]
+        pos = mla.q_pos(s)
+        ref = oracle.indexer_scores(idx.q_idx[a:b], idx.w[a:b], kc, ks, pos)
+        L = int(mla.total_len[s])
+        got = sc[a:b, :L]
+        fin = np.isfinite(ref)
+        assert np.array_equal(fin, np.isfinite(got))
+        assert np.all(sc[a:b, L:] == -np.inf)
+        err = np.abs(got[fin] - ref[fin])
+        scale_ref = np.abs(ref[fin]).max()
+        print(f"indexer H={H} seq={s}: max_abs={err.max():.3e} (ref max {scale_ref:.2f})")
+        assert err.max() <= 2e-3 * scale_ref
+        for r in range(b - a):
+            exact = oracle.topk_indices(got[r], pos[r] + 1, k)
+            assert np.array_equal(topk[a + r], exact), (s, r)
+            # against the oracle's own scores: any difference is a near-tie at the k-th score
+            oref = oracle.topk_indices(ref[r], pos[r] + 1, k)
+            diff = np.setxor1d(oref[oref >= 0], topk[a + r][topk[a + r] >= 0])
+            if diff.size:
+                kth = np.sort(ref[r][:pos[r] + 1])[::-1][min(k, pos[r] + 1) - 1]
+                assert np.all(np.abs(ref[r][diff] - kth) <= 2 * err.max() + 1e-12)
+
+
+def test_sparse_mla(pa_lib):
+    import torch
+    lengths, n_new = [3000 + 50, 700 + 20], [50, 20]
+    mla, idx = W.make_sparse_mla(91, lengths=lengths, n_new=n_new, num_q_heads=64)
+    dev = MlaOnDevice(mla, idx)
+    k = 512
+    topk, _ = _indexer(pa_lib, dev, k)
+    out = pa_lib.sparse_mla_attn(dev.q, dev.pool, dev.bt, dev.q_seq, topk, scale=mla.scale)
+    torch.cuda.synchronize()
+    got = bf16_out(out)
+    tk = topk.cpu().numpy()
+    for s in range(2):
+        L = int(mla.total_len[s])
+        codes = oracle.gather_paged(mla.kv_pool, mla.block_table[s], L)
+        sc = oracle.gather_paged(mla.kv_scale[..., None], mla.block_table[s], L)[:, 0]
+        a, b = mla.q_start[s], mla.q_start[s + 1]
+        ro, _ = oracle.sparse_mla_attention(mla.q[a:b], codes, sc, tk[a:b], mla.scale)
+        assert_close(got[a:b], ro, FP8_MAX_ABS, FP8_L1, f"sparse seq={s}")
+
+
+def test_sparse_mla_k_covers_context_equals_dense(pa_lib):
+    """k >= context: the sparse path must reproduce dense MLA (GLM-5.3 report, 'How to try')."""
+    import torch
+    mla, idx = W.make_sparse_mla(92, lengths=[300], n_new=[40], num_q_heads=64)
+    dev = MlaOnDevice(mla, idx)
+    topk, _ = _indexer(pa_lib, dev, 512)
+    tk = topk.cpu().numpy()
+    pos = mla.q_pos(0)
+    for r in range(40):
+        assert np.array_equal(tk[r][:pos[r] + 1], np.arange(pos[r] + 1)) and np.all(tk[r][pos[r] + 1:] == -1)
+    out = pa_lib.sparse_mla_attn(dev.q, dev.pool, dev.bt, dev.q_seq, topk, scale=mla.scale)
+    torch.cuda.synchronize()
+    (ro, _), _, _ = _mla_ref(mla, 0)
+    assert_close(bf16_out(out), ro, FP8_MAX_ABS, FP8_L1, "sparse == dense")
