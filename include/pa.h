@@ -230,6 +230,23 @@ pa_status pa_test_topk_from_scores(const float* scores, const int32_t* valid_len
                                    int32_t* out_idx, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
 
+/* ---------------------------------------------------------------------------------
+ * Profiling hooks (not part of the serving path).
+ *
+ * pa_profile_enable(max_records): from now on, every kernel the library launches (up to
+ *   max_records launches) is bracketed by two hipEvents recorded on the call's stream.
+ *   Creates 2*max_records events (no device memory is allocated); resets the records.
+ * pa_profile_count(): number of launches recorded so far.
+ * pa_profile_record(i, name, cap, ms): waits for record i and returns its kernel name
+ *   ("prefill_gqa", "decode_gqa", "decode_mla", "combine", "indexer", "topk",
+ *   "sparse_mla") and its duration in milliseconds.
+ * pa_profile_disable(): stops recording and destroys the events.
+ * ------------------------------------------------------------------------------- */
+pa_status pa_profile_enable(int32_t max_records);
+int32_t pa_profile_count(void);
+pa_status pa_profile_record(int32_t i, char* name_out, int32_t name_cap, float* ms_out);
+pa_status pa_profile_disable(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,8 @@ import os
 
 __all__ = ["load", "PAError", "KVPool", "gqa_pool", "mla_pool", "indexer_pool",
            "paged_attn_prefill", "paged_attn_decode", "mla_indexer_topk", "sparse_mla_attn",
-           "pa_test_gather_kv", "pa_test_topk_from_scores", "LIB_PATH"]
+           "pa_test_gather_kv", "pa_test_topk_from_scores", "pa_profile_enable",
+           "pa_profile_records", "pa_profile_disable", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 PA_BF16, PA_FP8_E4M3 = 1, 2
@@ -57,6 +58,10 @@ _SIGS = {
     "pa_test_gather_kv": (_c_i32, [_vp, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp]),
     "pa_test_topk_workspace_size": (_c_sz, [_c_i32, _c_i32]),
     "pa_test_topk_from_scores": (_c_i32, [_vp, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, _vp]),
+    "pa_profile_enable": (_c_i32, [_c_i32]),
+    "pa_profile_count": (_c_i32, []),
+    "pa_profile_record": (_c_i32, [_c_i32, ctypes.c_char_p, _c_i32, ctypes.POINTER(_c_f)]),
+    "pa_profile_disable": (_c_i32, []),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -200,6 +205,26 @@ def sparse_mla_attn(q, pool: KVPool, block_table, q_seq, topk_idx, *, scale: flo
                                _p(q_seq), _p(topk_idx), n_q, k, Hq, scale, _p(out), _p(lse), None, 0,
                                _stream(q)), "sparse_mla_attn")
     return out
+
+
+def pa_profile_enable(max_records: int) -> None:
+    _check(load().pa_profile_enable(max_records), "pa_profile_enable")
+
+
+def pa_profile_records():
+    """[(kernel name, milliseconds)] for every launch recorded since pa_profile_enable."""
+    lib = load()
+    out = []
+    buf = ctypes.create_string_buffer(64)
+    ms = _c_f()
+    for i in range(lib.pa_profile_count()):
+        _check(lib.pa_profile_record(i, buf, 64, ctypes.byref(ms)), "pa_profile_record")
+        out.append((buf.value.decode(), float(ms.value)))
+    return out
+
+
+def pa_profile_disable() -> None:
+    load().pa_profile_disable()
 
 
 def pa_test_gather_kv(pool: KVPool, block_table, seq: int, n_tokens: int, k_out, v_out=None,

@@ -17,9 +17,10 @@
 //   * computes S with v_mfma_f32_16x16x32_bf16 (Q rows r at MFMA row 4r when T*G <= 4,
 //     so every lane holds a real score in register 0);
 //   * updates the running max / sum with 16-lane reductions and exp2;
-//   * writes V^T (dims x keys) into its LDS slice -- V arrives 4 tokens x 8 dims per
-//     lane and is transposed in registers -- and P into LDS, then accumulates
-//     O^T += V^T P^T with v_mfma_f32_16x16x32_bf16.
+//   * writes V^T (dims x keys, fp16: exact conversion) into its LDS slice -- V arrives
+//     4 tokens x 8 dims per lane and is transposed in registers; rows past the context
+//     are zeros -- and P (fp16) into LDS, then accumulates O^T += V^T P^T with
+//     v_mfma_f32_16x16x32_f16.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(GqaDecodeArgs a) {
       if (pb >= 0) {
         const uint16_t* vp = a.v + ((size_t)pb * Hkv + g) * head_stride + (size_t)(4 * (kg & 3)) * D + 8 * dc;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vr[j][e] = ld16(vp + (size_t)e * D);
+        for (int e = 0; e < 4; ++e) vr[j][e] = (kb + 4 * kg + e < L) ? ld16(vp + (size_t)e * D) : u32x4{0, 0, 0, 0};
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) vr[j][e] = u32x4{0, 0, 0, 0};
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(GqaDecodeArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) sacc[st] = mfma16x16x32(qa[ks], kf[st][ks], sacc[st]);
     }
-    // ---- online softmax (log2 domain); P -> LDS as bf16 [row][key]
+    // ---- online softmax (log2 domain); P -> LDS as fp16 [row][key]
     float alpha[NREG];
 #pragma unroll
     for (int i = 0; i < NREG; ++i) {
@@ -144,14 +145,18 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(GqaDecodeArgs a) {
       l_run[i] = l_run[i] * alpha[i] + p0 + p1;
       m_run[i] = m_new;
       if (srow[i] < R) {
-        ps[srow[i] * kPStride + m16] = __builtin_bit_cast(uint16_t, (__bf16)p0);
-        ps[srow[i] * kPStride + 16 + m16] = __builtin_bit_cast(uint16_t, (__bf16)p1);
+        ps[srow[i] * kPStride + m16] = __builtin_bit_cast(uint16_t, (_Float16)p0);
+        ps[srow[i] * kPStride + 16 + m16] = __builtin_bit_cast(uint16_t, (_Float16)p1);
       }
     }
     // ---- V^T -> LDS: transpose (4 keys x 8 dims) per group in registers
 #pragma unroll
     for (int j = 0; j < VG; ++j) {
       const int gi = lane + 64 * j, kg = gi & 7, dc = gi >> 3;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) vr[j][e][w] = bf16x2_to_f16x2(vr[j][e][w]);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         u32x2 lo, hi;
@@ -186,7 +191,7 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(GqaDecodeArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const u32x4 va = *reinterpret_cast<const u32x4*>(vt + (m16 + 16 * mt) * kVtStride + 8 * grp);
-      acc[mt] = mfma16x16x32(va, pb, acc[mt]);
+      acc[mt] = mfma16x16x32_f16(va, pb, acc[mt]);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();

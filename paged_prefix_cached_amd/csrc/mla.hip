@@ -13,13 +13,14 @@
 // 32-key tile is staged once in LDS for all 64 rows:
 //   * keys are gathered through the block table (decode: a contiguous key range;
 //     sparse: the query's selected positions), 4 tokens x 16 bytes per thread;
-//   * FP8 E4M3 is upcast exactly to bf16 (hardware converter), stored row-major for the
-//     QK operand and transposed (dims x keys) for the PV operand;
+//   * FP8 E4M3 is upcast exactly (hardware converter) to bf16, stored row-major for the
+//     QK operand (queries are bf16), and to fp16, stored transposed (dims x keys) for
+//     the PV operand (P in fp16 keeps 11 significant bits);
 //   * the per-token fp32 scale is folded into the scores (s = scale_t * q.k) and into
 //     the probabilities used for PV (p * scale_t), never into the stored bf16;
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (Q^T in registers, 18 k-steps), online
-//     softmax on the C tile (one query row per lane), O^T += V^T P^T with the
-//     probabilities fed from registers.
+//     softmax on the C tile (one query row per lane), O^T += V^T P^T
+//     (v_mfma_f32_16x16x32_f16) with the probabilities fed from registers.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -150,6 +151,8 @@ __global__ __launch_bounds__(256, 1) void mla_kernel(MlaDecodeArgs da, SparseMla
         }
         if (dc < kDv / 16) {
           uint16_t* vrow = sm.vt + (16 * dc + 4 * w4) * kVtStride + 4 * kg;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) c[e] = fp8x4_to_f16x4(raw[e][w4]);
           u32x2 t;
           t.x = __builtin_amdgcn_perm(c[1].x, c[0].x, 0x05040100u);
           t.y = __builtin_amdgcn_perm(c[3].x, c[2].x, 0x05040100u);
@@ -206,8 +209,8 @@ __global__ __launch_bounds__(256, 1) void mla_kernel(MlaDecodeArgs da, SparseMla
           rs += p;
           pv[4 * st + i] = p * sm.vs[16 * st + 4 * grp + i];
         }
-      pb = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                 pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+      pb = u32x4{pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]),
+                 pack_f16x2(pv[4], pv[5]), pack_f16x2(pv[6], pv[7])};
     } else {
       pb = u32x4{0, 0, 0, 0};
     }
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(256, 1) void mla_kernel(MlaDecodeArgs da, SparseMla
       const uint16_t* vp = sm.vt + (16 * mt + m16) * kVtStride + 4 * grp;
       const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
       const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 16);
-      acc[mt] = mfma16x16x32(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, acc[mt] * alpha);
+      acc[mt] = mfma16x16x32_f16(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, acc[mt] * alpha);
     }
   }
 

@@ -5,6 +5,8 @@
 #include <string.h>
 
 #include <cmath>
+#include <mutex>
+#include <vector>
 
 #include "../../include/pa.h"
 #include "pa_internal.h"
@@ -58,6 +60,32 @@ pa_status check_fp8_pool(const pa_kv_pool* p, int d_qk, int d_v, const char* wha
 pa_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return PA_OK;
+}
+
+// ---- optional per-launch timing (pa_profile_*): events recorded on the call's stream
+struct ProfRec {
+  const char* name;
+  int slot;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<hipEvent_t> g_prof_events;   // 2 per record slot
+std::vector<ProfRec> g_prof_recs;
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
+  int slot = -1;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (g_prof_on && g_prof_recs.size() * 2 < g_prof_events.size()) {
+      slot = (int)g_prof_recs.size();
+      g_prof_recs.push_back({name, slot});
+    }
+  }
+  if (slot >= 0) hipEventRecord(g_prof_events[2 * slot], stream);
+  const hipError_t e = launch();
+  if (slot >= 0) hipEventRecord(g_prof_events[2 * slot + 1], stream);
+  return e;
 }
 
 #define PA_TRY(x)                       \
@@ -159,7 +187,7 @@ pa_status paged_attn_prefill(const void* q, const pa_kv_pool* pool, const int32_
   a.max_total_len = max_total_len;
   a.scale_log2 = scale * 1.4426950408889634f;
   (void)hipGetLastError();
-  return launched(pa::launch_gqa_prefill(a, stream), "prefill launch");
+  return launched(timed("prefill_gqa", stream, [&] { return pa::launch_gqa_prefill(a, stream); }), "prefill launch");
 }
 
 // ------------------------------------------------------------------------- decode
@@ -235,7 +263,7 @@ pa_status paged_attn_decode(const void* q, const pa_kv_pool* pool, const int32_t
     a.max_context_len = max_context_len;
     a.max_splits = l.max_splits;
     a.scale_log2 = scale * 1.4426950408889634f;
-    PA_TRY(launched(pa::launch_gqa_decode(a, stream), "decode launch"));
+    PA_TRY(launched(timed("decode_gqa", stream, [&] { return pa::launch_gqa_decode(a, stream); }), "decode launch"));
   } else {
     pa::MlaDecodeArgs a{};
     a.q = static_cast<const uint16_t*>(q);
@@ -253,7 +281,7 @@ pa_status paged_attn_decode(const void* q, const pa_kv_pool* pool, const int32_t
     a.max_context_len = max_context_len;
     a.max_splits = l.max_splits;
     a.scale_log2 = scale * 1.4426950408889634f;
-    PA_TRY(launched(pa::launch_mla_decode(a, stream), "MLA decode launch"));
+    PA_TRY(launched(timed("decode_mla", stream, [&] { return pa::launch_mla_decode(a, stream); }), "MLA decode launch"));
   }
   pa::CombineArgs c{};
   c.part_o = part_o;
@@ -267,7 +295,7 @@ pa_status paged_attn_decode(const void* q, const pa_kv_pool* pool, const int32_t
   c.max_splits = l.max_splits;
   c.split = l.split;
   c.max_context_len = max_context_len;
-  return launched(pa::launch_combine(c, stream), "combine launch");
+  return launched(timed("combine", stream, [&] { return pa::launch_combine(c, stream); }), "combine launch");
 }
 
 // ------------------------------------------------------------------------- indexer + top-k
@@ -331,7 +359,7 @@ pa_status mla_indexer_topk(const void* q_idx, const float* w, const pa_kv_pool* 
   a.max_new_len = max_new_len;
   a.max_total_len = max_total_len;
   a.score_stride = max_total_len;
-  PA_TRY(launched(pa::launch_indexer_scores(a, stream), "indexer launch"));
+  PA_TRY(launched(timed("indexer", stream, [&] { return pa::launch_indexer_scores(a, stream); }), "indexer launch"));
   pa::TopkArgs t{};
   t.scores = scores;
   t.valid_len = valid;
@@ -340,7 +368,7 @@ pa_status mla_indexer_topk(const void* q_idx, const float* w, const pa_kv_pool* 
   t.row_stride = max_total_len;
   t.k = k;
   t.max_valid = max_total_len;
-  return launched(pa::launch_topk(t, stream), "top-k launch");
+  return launched(timed("topk", stream, [&] { return pa::launch_topk(t, stream); }), "top-k launch");
 }
 
 // ------------------------------------------------------------------------- sparse MLA
@@ -380,7 +408,7 @@ pa_status sparse_mla_attn(const void* q, const pa_kv_pool* pool, const int32_t* 
   a.num_q_heads = num_q_heads;
   a.num_blocks = pool->num_blocks;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return launched(pa::launch_sparse_mla(a, stream), "sparse MLA launch");
+  return launched(timed("sparse_mla", stream, [&] { return pa::launch_sparse_mla(a, stream); }), "sparse MLA launch");
 }
 
 // ------------------------------------------------------------------------- test hooks
@@ -441,7 +469,51 @@ pa_status pa_test_topk_from_scores(const float* scores, const int32_t* valid_len
   t.row_stride = row_stride;
   t.k = k;
   t.max_valid = row_stride;
-  return launched(pa::launch_topk(t, stream), "top-k launch");
+  return launched(timed("topk", stream, [&] { return pa::launch_topk(t, stream); }), "top-k launch");
+}
+
+// ------------------------------------------------------------------------- profiling
+pa_status pa_profile_enable(int32_t max_records) {
+  g_detail[0] = 0;
+  if (max_records < 1 || max_records > (1 << 20)) return fail(PA_ERR_INVALID_ARG, "max_records must be 1..2^20");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (hipEvent_t e : g_prof_events) (void)hipEventDestroy(e);
+  g_prof_events.assign(2 * (size_t)max_records, nullptr);
+  for (auto& e : g_prof_events)
+    if (hipEventCreate(&e) != hipSuccess) {
+      g_prof_events.clear();
+      return fail(PA_ERR_HIP, "hipEventCreate failed");
+    }
+  g_prof_recs.clear();
+  g_prof_on = true;
+  return PA_OK;
+}
+
+int32_t pa_profile_count(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  return (int32_t)g_prof_recs.size();
+}
+
+pa_status pa_profile_record(int32_t i, char* name_out, int32_t name_cap, float* ms_out) {
+  g_detail[0] = 0;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (i < 0 || i >= (int32_t)g_prof_recs.size() || ms_out == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "no profile record %d", i);
+  const ProfRec& r = g_prof_recs[i];
+  if (name_out && name_cap > 0) snprintf(name_out, (size_t)name_cap, "%s", r.name);
+  if (hipEventSynchronize(g_prof_events[2 * r.slot + 1]) != hipSuccess ||
+      hipEventElapsedTime(ms_out, g_prof_events[2 * r.slot], g_prof_events[2 * r.slot + 1]) != hipSuccess)
+    return fail(PA_ERR_HIP, "event timing failed");
+  return PA_OK;
+}
+
+pa_status pa_profile_disable(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = false;
+  for (hipEvent_t e : g_prof_events) (void)hipEventDestroy(e);
+  g_prof_events.clear();
+  g_prof_recs.clear();
+  return PA_OK;
 }
 
 }  // extern "C"

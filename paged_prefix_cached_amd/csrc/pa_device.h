@@ -18,6 +18,8 @@
 namespace pa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -36,6 +38,42 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// fp16 variants, used for P.V: probabilities in [0, 1] keep 11 significant bits in fp16
+// (8 in bf16), and V converts to fp16 exactly (see below).
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16_f16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Two floats -> packed fp16x2, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// Packed bf16x2 -> packed fp16x2.  Exact for |x| in [2^-14, 65504] (8 significant bits fit
+// in 11); smaller magnitudes become fp16 subnormals (absolute error < 2^-25) and larger
+// ones saturate to +-65504 (round toward zero never overflows to infinity).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t u) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(u << 16),
+                                                                  __uint_as_float(u & 0xffff0000u)));
+}
+
+// Four OCP E4M3FN bytes -> four fp16, exact (every E4M3 value is an fp16 normal).
+__device__ __forceinline__ u32x2 fp8x4_to_f16x4(uint32_t src) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)src, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)src, true);
+  u32x2 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo.x, lo.y));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi.x, hi.y));
+  return r;
 }
 
 // Two floats -> packed bf16x2 (round to nearest even).

@@ -10,12 +10,14 @@
 // table in 64-key tiles (four 16-token blocks):
 //   * the whole workgroup loads the next tile from HBM into registers while the current
 //     one is computed (coalesced 16-byte loads; a (block, head) tile is contiguous);
-//   * K goes to LDS row-major (padded rows), V goes to LDS transposed (dims x keys),
-//     transposed in registers 4 keys x 8 dims at a time;
+//   * K goes to LDS row-major (padded rows) as bf16; V goes to LDS transposed (dims x
+//     keys) as fp16 (exact conversion), transposed in registers 4 keys x 8 dims at a
+//     time; V rows past the sequence end are stored as zeros;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: Q^T stays in registers for the whole
 //     loop; in the C layout each lane holds one query row, so the online softmax needs
-//     a single cross-lane step and the probabilities feed O^T += V^T P^T directly as
-//     the B operand, in the same register order as the V^T fragments read from LDS.
+//     a single cross-lane step and the probabilities (rounded to fp16, which keeps 11
+//     significant bits) feed O^T += V^T P^T (v_mfma_f32_32x32x16_f16) directly as the B
+//     operand, in the same register order as the V^T fragments read from LDS.
 // Workgroups of the same (sequence, KV head) are mapped onto one XCD so its L2 serves
 // the shared prefix to all of them.
 #include "pa_device.h"
@@ -109,7 +111,8 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
       if (pb >= 0) {
         const uint16_t* vp = a.v + ((size_t)pb * Hkv + g) * head_stride + (size_t)((4 * kg) & 15) * D + 8 * dc;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vreg[e] = ld16(vp + (size_t)e * D);
+        for (int e = 0; e < 4; ++e)
+          vreg[e] = (kt + 4 * kg + e < total) ? ld16(vp + (size_t)e * D) : u32x4{0, 0, 0, 0};
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) vreg[e] = u32x4{0, 0, 0, 0};
@@ -125,6 +128,10 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
     }
     if (tid < VGR) {
       const int kg = tid % (kKT / 4), dc = tid / (kKT / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) vreg[e][w] = bf16x2_to_f16x2(vreg[e][w]);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         u32x2 lo, hi;
@@ -199,17 +206,17 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
     for (int ks = 0; ks < 4; ++ks) {
       const int st = ks >> 1, r0 = 8 * (ks & 1);
       u32x4 pb;
-      pb.x = pack_bf16x2(sacc[st][r0 + 0], sacc[st][r0 + 1]);
-      pb.y = pack_bf16x2(sacc[st][r0 + 2], sacc[st][r0 + 3]);
-      pb.z = pack_bf16x2(sacc[st][r0 + 4], sacc[st][r0 + 5]);
-      pb.w = pack_bf16x2(sacc[st][r0 + 6], sacc[st][r0 + 7]);
+      pb.x = pack_f16x2(sacc[st][r0 + 0], sacc[st][r0 + 1]);
+      pb.y = pack_f16x2(sacc[st][r0 + 2], sacc[st][r0 + 3]);
+      pb.z = pack_f16x2(sacc[st][r0 + 4], sacc[st][r0 + 5]);
+      pb.w = pack_f16x2(sacc[st][r0 + 6], sacc[st][r0 + 7]);
       const int kbase = 32 * st + 16 * (ks & 1) + 4 * h32;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const uint16_t* vp = sm.vt + (32 * mt + c32) * Sm::vtStride + kbase;
         const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
         const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
-        acc[mt] = mfma32x32x16(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, acc[mt]);
+        acc[mt] = mfma32x32x16_f16(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, acc[mt]);
       }
     }
   }

@@ -9,7 +9,7 @@ import pytest
 import oracle
 import workloads as W
 from workloads.device import GqaOnDevice
-from gpu_util import BF16_L1, BF16_MAX_ABS, LSE_ABS, assert_close, bf16_out
+from gpu_util import BF16_L1, BF16_MAX_ABS, LSE_ABS, assert_close, assert_close_stress, bf16_out
 
 pytestmark = pytest.mark.gpu
 
@@ -78,7 +78,7 @@ def test_prefill_peaked_softmax(pa_lib):
     got = bf16_out(out)
     for s in range(2):
         ro, _ = oracle.paged_gqa_attention(wl, s)
-        assert_close(got[wl.q_start[s]:wl.q_start[s + 1]], ro, BF16_MAX_ABS, BF16_L1, f"peaked seq={s}")
+        assert_close_stress(got[wl.q_start[s]:wl.q_start[s + 1]], ro, BF16_MAX_ABS, BF16_L1, f"peaked seq={s}")
 
 
 def _decode(pa, dev, T, lse=True):
