@@ -88,13 +88,13 @@ def decode_bytes(wl):
     return unique, logical, qo
 
 
-def bench_decode(args, dev_name):
+def bench_decode(args, dev_name, share=True):
     import torch
     import paged_prefix_cached_amd as pa
     import workloads as W
     from workloads.device import GqaOnDevice
     t = time.time()
-    wl = W.make_gqa_decode(2)
+    wl = W.make_gqa_decode(2, share=share)
     dev = GqaOnDevice(wl)
     log(f"[bench] decode workload ready in {time.time() - t:.1f}s")
     S, H, D = wl.num_seqs, wl.num_q_heads, wl.head_dim
@@ -259,9 +259,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--secondary", default="", help="comma list of extra workloads: 3 (prefill), "
-                                                    "4 (MLA MTP3 decode), 5 (indexer + sparse MLA)")
+    ap.add_argument("--secondary", default="", help="comma list of extra workloads: 2n (decode with no "
+                                                    "shared blocks), 3 (prefill), 4 (MLA MTP3 decode), "
+                                                    "5 (indexer + sparse MLA)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one 1 GiB device-to-device copy (reference kernel for HBM counters)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -275,6 +278,13 @@ def main():
     import paged_prefix_cached_amd as pa
     pa.load()
     dev_name = torch.cuda.get_device_name(0)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     res, wl = bench_decode(args, dev_name)
     line = {"metric": METRIC, "value": res["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
@@ -284,6 +294,11 @@ def main():
     if args.secondary:
         sec = {}
         for c in [x.strip() for x in args.secondary.split(",") if x.strip()]:
+            if c == "2n":   # control: the same decode batch with no shared blocks
+                r, _ = bench_decode(args, dev_name, share=False)
+                sec["decode_no_sharing"] = {k: r[k] for k in ("ms_per_step", "value", "unique_kv_gbps",
+                                                              "tokens_per_s", "kernel_ms", "roofline")}
+                continue
             f = {"3": ("prefill_suffix", bench_prefill), "4": ("mla_decode_mtp3", bench_mla),
                  "5": ("indexer_topk_sparse_mla", bench_sparse)}[c]
             sec[f[0]] = f[1](max(2, args.steps // 4), max(1, args.warmup // 2))

@@ -95,6 +95,18 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t src) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ds_read_b64_tr_b16 (LDS transpose read, 16-bit elements).  Within each group of 16
+// lanes, lane n receives element n%4 of the 8-byte reads of lanes 4j + n/4 (j = 0..3).  So
+// when lane m of a group reads 4 consecutive elements at row r0 + m/4, column c0 + 4*(m%4)
+// of a row-major LDS matrix, lane n gets column c0 + n of rows r0 .. r0+3: a 4 x 16 block
+// arrives transposed, one column per lane -- the MFMA operand layout with the reduction
+// index (rows) in the lane's registers.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  auto* lp = (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) uint16_t*)p);
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
+}
+
 // Unaligned-free 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

@@ -8,8 +8,14 @@ namespace pa {
 
 // Keys per split of the decode key range.  Each split yields a partial (o, lse) pair
 // that the combine kernel merges in split order.
-constexpr int kDecodeSplitGqa = 1024;
-constexpr int kDecodeSplitMla = 8192;
+#ifndef PA_DECODE_SPLIT_GQA
+#define PA_DECODE_SPLIT_GQA 1024
+#endif
+#ifndef PA_DECODE_SPLIT_MLA
+#define PA_DECODE_SPLIT_MLA 8192
+#endif
+constexpr int kDecodeSplitGqa = PA_DECODE_SPLIT_GQA;
+constexpr int kDecodeSplitMla = PA_DECODE_SPLIT_MLA;
 
 struct GqaPrefillArgs {
   const uint16_t* q;

