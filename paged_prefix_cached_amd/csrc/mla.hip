@@ -32,9 +32,6 @@
 // accumulator is rescaled only when a row's running maximum grows.
 #include <type_traits>
 
-#ifndef PA_MLA_DECODE_PAIRS
-#define PA_MLA_DECODE_PAIRS 4
-#endif
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -45,13 +42,12 @@ namespace {
 constexpr int kDqk = 576, kDv = 512, kBs = 64;
 constexpr int kKT = 32;                   // keys per tile
 constexpr int kKS = 608;                  // fp16 per LDS row: 1,216 B, 304 dwords = 48 mod 64
-constexpr int kQH = kDqk / 32;            // 18 QK k-steps of 16 per wave (half of 576)
-constexpr int kMH = kDv / 64;             // 8 O^T tiles of 32 dims per wave (half of 512)
 constexpr int kChunks = kKT * (kDqk / 16);   // 16-byte FP8 chunks per tile (1,152)
 constexpr int kWaveLoads = kChunks / 64;     // 1 KB DMA wave-loads per tile (18)
 constexpr int kBtLds = 4096;              // block-table entries staged in LDS (sparse)
 constexpr int kSelLds = 2048;             // selected positions staged in LDS (sparse)
 static_assert(kChunks % 64 == 0, "tile is a whole number of wave-loads");
+static_assert(kKS >= kDqk + 16, "row 0's padding takes the discarded chunk slots");
 
 template <int N>
 using Int = std::integral_constant<int, N>;
@@ -62,21 +58,36 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
 __device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 4, 0, 0);
 }
-// Wait until at most N vector-memory operations of this wave are outstanding (gfx9
-// s_waitcnt encoding; expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+// Wait until no vector-memory operation of this wave is outstanding (gfx9 s_waitcnt
+// encoding: vmcnt 0, expcnt and lgkmcnt left at their maxima).
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+// Workgroup barrier that orders LDS accesses only.  A full __syncthreads() also waits for
+// outstanding vector-memory operations -- here the LDS-DMA of a later tile, still in
+// flight on purpose.
+// (An LDS-scoped fence is no help: LDS-DMA writes count as LDS writes, so it waits for
+// them too.)  The compiler-level memory clobbers keep LDS accesses on their side of it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-template <bool SPARSE, int NP>
-__global__ __launch_bounds__(NP * 128, 1) void mla_kernel(MlaDecodeArgs da, SparseMlaArgs sa) {
-  constexpr int NW = 2 * NP, NT = NW * 64;
-  // DMA operations per wave per tile: wave-loads w, w + NW, ...; the last wave also
-  // fetches the 32 scales.  MIN_OPS is the fewest any wave issues.
-  constexpr int MIN_OPS = kWaveLoads / NW;
-  static_assert(MIN_OPS >= 1 && MIN_OPS < 64, "DMA accounting");
+// NW waves per workgroup; SPLIT waves share each group of 32 query rows (1: a wave holds
+// all 576 Q dims and all 512 output dims; 2 or 4: the waves split both, exchanging
+// partial S through LDS).  STAGED (sparse only): the selected positions (k <= 2048) and the
+// sequence's block-table row (<= 4096 entries) are copied to LDS once; otherwise they
+// are read from global memory (a separate instantiation, so no lookup ever becomes a
+// flat access).  LATE_CONV: the upcast of tile t+1 runs interleaved with the P.V of tile
+// t (pays off with one wave a SIMD and registers to spare) instead of at the start of
+// step t.
+template <bool SPARSE, int NW, int SPLIT, bool STAGED, bool LATE_CONV>
+__global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, SparseMlaArgs sa) {
+  constexpr int NT = NW * 64;
+  constexpr int RW = 32 * NW / SPLIT;       // query rows per workgroup
+  constexpr int kQW = 36 / SPLIT;           // QK k-steps of 16 dims per wave
+  constexpr int kMW = 16 / SPLIT;           // O^T tiles of 32 dims per wave
+  static_assert(SPLIT == 1 || SPLIT == 2 || SPLIT == 4, "split");
   // The raw DMA targets are LDS objects of their own: the compiler then knows that reads
   // of the fp16 tiles (and of the other raw buffer) never alias a buffer the DMA is
   // filling, and inserts no wait for them.
@@ -90,13 +101,15 @@ __global__ __launch_bounds__(NP * 128, 1) void mla_kernel(MlaDecodeArgs da, Spar
   __shared__ __attribute__((aligned(16))) int32_t fk[2][kKT];    // position, -1 if invalid
   __shared__ __attribute__((aligned(16))) float fks[2][kKT];     // scale * softmax scale * log2 e
   __shared__ __attribute__((aligned(16))) float fvs[2][kKT];     // scale
-  __shared__ __attribute__((aligned(16))) f32x4 xs[NW * 4 * 64]; // partial S exchange
-  __shared__ int32_t bt_s[SPARSE ? kBtLds : kDecodeSplitMla / kBs + 1];
-  __shared__ int32_t sel_s[SPARSE ? kSelLds : 1];
+  __shared__ int32_t fall[2];                                    // 1: every key of the tile valid
+  __shared__ __attribute__((aligned(16))) f32x4 xs[SPLIT > 1 ? NW * 4 * 64 : 1];  // partial S
+  __shared__ int32_t bt_s[SPARSE ? (STAGED ? kBtLds : 1) : kDecodeSplitMla / kBs + 1];
+  __shared__ int32_t sel_s[SPARSE && STAGED ? kSelLds : 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, h = lane >> 5;
-  const int pair = wave >> 1, half = wave & 1;
+  const int grp32 = wave / SPLIT;                    // which 32 rows
+  const int half = wave % SPLIT;                     // which share of the dims
 
   // ---- work unit
   const uint16_t* qbase;
@@ -106,13 +119,12 @@ __global__ __launch_bounds__(NP * 128, 1) void mla_kernel(MlaDecodeArgs da, Spar
   const float* kv_scale;
   int Hq, n_keys, k_begin = 0, n_lblocks, L = 0, T = 1, row0, unit = 0, unit_split = 0;
   int lb_base = 0, n_bt, num_blocks;
-  bool bt_in_lds = true, sel_in_lds = true;
   float scale_log2;
   if constexpr (SPARSE) {
     Hq = sa.num_q_heads;
-    const int rblocks = (Hq + 32 * NP - 1) / (32 * NP);
+    const int rblocks = (Hq + RW - 1) / RW;
     const int i = blockIdx.x / rblocks;
-    row0 = (blockIdx.x % rblocks) * 32 * NP;
+    row0 = (blockIdx.x % rblocks) * RW;
     unit = i;
     qbase = sa.q + (size_t)i * Hq * kDqk;
     kv = sa.kv; kv_scale = sa.kv_scale; num_blocks = sa.num_blocks;
@@ -120,21 +132,19 @@ __global__ __launch_bounds__(NP * 128, 1) void mla_kernel(MlaDecodeArgs da, Spar
     sel_g = sa.topk + (size_t)i * sa.k;
     n_keys = sa.k;
     n_lblocks = sa.bt_stride;
-    bt_in_lds = sa.bt_stride <= kBtLds;
-    sel_in_lds = sa.k <= kSelLds;
-    n_bt = bt_in_lds ? sa.bt_stride : 0;
+    n_bt = STAGED ? sa.bt_stride : 0;
     scale_log2 = sa.scale_log2;
   } else {
     Hq = da.num_q_heads;
     T = da.q_per_seq;
     const int rows = T * Hq;
-    const int rblocks = (rows + 32 * NP - 1) / (32 * NP);
+    const int rblocks = (rows + RW - 1) / RW;
     const int n_units = da.num_seqs * da.max_splits * rblocks;
     const int logical = xcd_swizzle(blockIdx.x, n_units);
     const int rb = logical % rblocks;
     unit_split = (logical / rblocks) % da.max_splits;
     unit = logical / (rblocks * da.max_splits);
-    row0 = rb * 32 * NP;
+    row0 = rb * RW;
     L = min(da.context_len[unit], da.max_context_len);
     k_begin = unit_split * kDecodeSplitMla;
     if (k_begin >= L) return;                         // uniform for the workgroup
@@ -149,16 +159,16 @@ __global__ __launch_bounds__(NP * 128, 1) void mla_kernel(MlaDecodeArgs da, Spar
   }
   const int rows_total = SPARSE ? Hq : T * Hq;
 
-  // ---- this lane's query row (C column = lane % 32) and its half of the fp16 Q
-  const int row = row0 + pair * 32 + l32;
+  // ---- this lane's query row (C column = lane % 32) and its fp16 Q fragments
+  const int row = row0 + grp32 * 32 + l32;
   const bool row_ok = row < rows_total;
   const int row_c = row_ok ? row : rows_total - 1;
   const int pos = SPARSE ? 0x7fffffff : (L - T + row_c / Hq);
-  u32x4 qb[kQH];
+  u32x4 qb[kQW];
   {
-    const uint16_t* qp = qbase + (size_t)row_c * kDqk + 288 * half + 8 * h;
+    const uint16_t* qp = qbase + (size_t)row_c * kDqk + 16 * kQW * half + 8 * h;
 #pragma unroll
-    for (int ks = 0; ks < kQH; ++ks) {
+    for (int ks = 0; ks < kQW; ++ks) {
       const u32x4 v = ld16(qp + 16 * ks);
       qb[ks] = u32x4{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
     }
@@ -166,9 +176,8 @@ __global__ __launch_bounds__(NP * 128, 1) void mla_kernel(MlaDecodeArgs da, Spar
 
   // ---- stage validated block ids and, for sparse, the selected positions
   for (int j = tid; j < n_bt; j += NT) bt_s[j] = phys_block(bt_row, lb_base + j, n_lblocks, num_blocks);
-  if constexpr (SPARSE) {
-    if (sel_in_lds)
-      for (int j = tid; j < n_keys; j += NT) sel_s[j] = sel_g[j];
+  if constexpr (SPARSE && STAGED) {
+    for (int j = tid; j < n_keys; j += NT) sel_s[j] = sel_g[j];
   }
   __syncthreads();
   // j-th key of the unit -> physical block (or -1) and its logical position
@@ -176,18 +185,25 @@ __global__ __launch_bounds__(NP * 128, 1) void mla_kernel(MlaDecodeArgs da, Spar
     idx = -1;
     if (j >= n_keys) return -1;
     if constexpr (SPARSE) {
-      idx = sel_in_lds ? sel_s[j] : sel_g[j];
-      if (idx < 0) return -1;
-      const int lb = idx / kBs;
-      if (bt_in_lds) return lb < n_bt ? bt_s[lb] : -1;
-      return phys_block(bt_row, lb, n_lblocks, num_blocks);
+      if constexpr (STAGED) {
+        idx = sel_s[j];
+        if (idx < 0) return -1;
+        const int lb = idx / kBs;
+        return lb < n_bt ? bt_s[lb] : -1;
+      } else {
+        idx = sel_g[j];
+        if (idx < 0) return -1;
+        return phys_block(bt_row, idx / kBs, n_lblocks, num_blocks);
+      }
     } else {
       idx = k_begin + j;
       return bt_s[idx / kBs - lb_base];
     }
   };
 
-  // ---- stage 1: DMA tile tt into raw buffer P
+  // ---- stage 1: DMA tile tt into raw buffer P.  Raw chunk c (16 bytes: key c / 36,
+  // dims 16 (c % 36) ..) lands at R + 16 c; wave-load j covers chunks 64 j .. 64 j + 63.
+  constexpr int kLoadsPerWave = (kWaveLoads + NW - 1) / NW;
   auto issue = [&](auto P, int tt) {
     uint8_t* R = P ? r1 : r0;
     float* RS = P ? rs1 : rs0;
@@ -195,60 +211,116 @@ __global__ __launch_bounds__(NP * 128, 1) void mla_kernel(MlaDecodeArgs da, Spar
     const int kb = tt * kKT;
     int ln = lane;
     asm volatile("" : "+v"(ln));   // recompute the lane's indices here, keep no VGPRs for them
-    for (int j = wave; j < kWaveLoads; j += NW) {
-      const int c = 64 * j + ln;
-      const int key = c / (kDqk / 16), dc = c % (kDqk / 16);
-      int idx;
-      const int pb = key_loc(kb + key, idx);
-      // invalid keys read a harmless in-bounds row; stage 2 replaces them by zeros
-      const uint8_t* src = pb >= 0 ? kv + ((size_t)pb * kBs + idx % kBs) * kDqk + 16 * dc : kv;
-      dma16(src, R + 1024 * j);
-    }
-    if (wave == NW - 1 && ln < kKT) {
-      int idx;
-      const int pb = key_loc(kb + ln, idx);
-      dma4(pb >= 0 ? kv_scale + (size_t)pb * kBs + idx % kBs : kv_scale, RS);
-      RK[ln] = pb >= 0 ? idx : -1;
+    if constexpr (!SPARSE) {
+      // a 32-key tile of a contiguous range never straddles a 64-token block: its FP8
+      // rows are one contiguous 18,432-byte span of one block
+      const int pos0 = k_begin + kb;
+      const int pb = bt_s[pos0 / kBs - lb_base];
+      const uint8_t* span = pb >= 0 ? kv + ((size_t)pb * kBs + pos0 % kBs) * kDqk : kv;
+#pragma unroll
+      for (int m = 0; m < kLoadsPerWave; ++m) {
+        const int j = wave + NW * m;
+        if (j < kWaveLoads) dma16(pb >= 0 ? span + 16 * (64 * j + ln) : kv, R + 1024 * j);
+      }
+      if (wave == NW - 1 && ln < kKT) {
+        dma4(pb >= 0 ? kv_scale + (size_t)pb * kBs + pos0 % kBs + ln : kv_scale, RS);
+        RK[ln] = (pb >= 0 && kb + ln < n_keys) ? pos0 + ln : -1;
+      }
+    } else {
+      // per-key lookups, all LDS reads issued before the DMAs
+      int idx[kLoadsPerWave], pbk[kLoadsPerWave];
+#pragma unroll
+      for (int m = 0; m < kLoadsPerWave; ++m) {
+        const int key = (64 * (wave + NW * m) + ln) / (kDqk / 16);
+        pbk[m] = key_loc(kb + key, idx[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < kLoadsPerWave; ++m) {
+        const int j = wave + NW * m;
+        const int dc = (64 * j + ln) % (kDqk / 16);
+        if (j < kWaveLoads)
+          dma16(pbk[m] >= 0 ? kv + ((size_t)pbk[m] * kBs + idx[m] % kBs) * kDqk + 16 * dc : kv, R + 1024 * j);
+      }
+      if (wave == NW - 1 && ln < kKT) {
+        int id;
+        const int pb = key_loc(kb + ln, id);
+        dma4(pb >= 0 ? kv_scale + (size_t)pb * kBs + id % kBs : kv_scale, RS);
+        RK[ln] = pb >= 0 ? id : -1;
+      }
     }
   };
-  // ---- stage 2: raw buffer P -> fp16 tile P (and its key metadata)
-  auto convert = [&](auto P) {
+  // ---- stage 2: raw buffer P -> fp16 tile P, unrolled with all LDS reads first.  With the
+  // late upcast it is also branch-free, so that it shares a basic block with -- and
+  // interleaves with -- the P.V MFMAs of the previous tile: chunk slots past the tile
+  // then write into row 0's padding (fp16 576 .. 591), which nothing reads.
+  constexpr int CPT = (kChunks + NT - 1) / NT;
+  auto convert_chunks = [&](auto P) {
     const uint8_t* R = P ? r1 : r0;
-    const float* RS = P ? rs1 : rs0;
     const int32_t* RK = P ? rk1 : rk0;
     uint16_t* F = fb[P];
     int th = tid;
     asm volatile("" : "+v"(th));
-    for (int c = th; c < kChunks; c += NT) {
+    u32x4 raw[CPT];
+    bool ok[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = th + NT * i;
+      const bool in = i < CPT - 1 || c < kChunks;
+      const int cc = in ? c : 0;
+      ok[i] = in && RK[cc / (kDqk / 16)] >= 0;
+      raw[i] = *reinterpret_cast<const u32x4*>(R + 16 * cc);
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = th + NT * i;
+      const bool in = i < CPT - 1 || c < kChunks;
       const int key = c / (kDqk / 16), dc = c % (kDqk / 16);
       const int v = (key >> 2) & 3;
-      u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-      if (RK[key] >= 0) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(R + 16 * c);
-        const u32x2 a0 = fp8x4_to_f16x4(raw.x), a1 = fp8x4_to_f16x4(raw.y);
-        const u32x2 a2 = fp8x4_to_f16x4(raw.z), a3 = fp8x4_to_f16x4(raw.w);
-        lo = u32x4{a0.x, a0.y, a1.x, a1.y};
-        hi = u32x4{a2.x, a2.y, a3.x, a3.y};
+      const u32x2 a0 = fp8x4_to_f16x4(raw[i].x), a1 = fp8x4_to_f16x4(raw[i].y);
+      const u32x2 a2 = fp8x4_to_f16x4(raw[i].z), a3 = fp8x4_to_f16x4(raw[i].w);
+      const u32x4 lo = ok[i] ? u32x4{a0.x, a0.y, a1.x, a1.y} : u32x4{0, 0, 0, 0};
+      const u32x4 hi = ok[i] ? u32x4{a2.x, a2.y, a3.x, a3.y} : u32x4{0, 0, 0, 0};
+      if constexpr (LATE_CONV) {   // branch-free: the discarded slots go to the padding
+        const int o_lo = in ? key * kKS + 8 * ((2 * dc) ^ v) : kDqk;
+        const int o_hi = in ? key * kKS + 8 * ((2 * dc + 1) ^ v) : kDqk + 8;
+        st16(F + o_lo, lo);
+        st16(F + o_hi, hi);
+      } else if (in) {
+        st16(F + key * kKS + 8 * ((2 * dc) ^ v), lo);
+        st16(F + key * kKS + 8 * ((2 * dc + 1) ^ v), hi);
       }
-      uint16_t* rp = F + key * kKS;
-      st16(rp + 8 * ((2 * dc) ^ v), lo);
-      st16(rp + 8 * ((2 * dc + 1) ^ v), hi);
     }
-    if (th < kKT) {
-      const int id = RK[th];
-      const float sc = RS[th];
-      fk[P][th] = id;
-      fks[P][th] = id >= 0 ? sc * scale_log2 : 0.f;
-      fvs[P][th] = id >= 0 ? sc : 0.f;
+  };
+  // key metadata of the tile in raw buffer P -> fp16 tile P's metadata (wave 0)
+  auto convert_meta = [&](auto P) {
+    const float* RS = P ? rs1 : rs0;
+    const int32_t* RK = P ? rk1 : rk0;
+    if (wave == 0) {
+      const int id = lane < kKT ? RK[lane] : 0;
+      const float sc = lane < kKT ? RS[lane] : 0.f;
+      if (lane < kKT) {
+        fk[P][lane] = id;
+        fks[P][lane] = id >= 0 ? sc * scale_log2 : 0.f;
+        fvs[P][lane] = id >= 0 ? sc : 0.f;
+      }
+      const bool all_valid = __ballot(id < 0) == 0;
+      if (lane == 0) fall[P] = all_valid ? 1 : 0;
     }
+  };
+  auto convert = [&](auto P) {
+    convert_chunks(P);
+    convert_meta(P);
   };
 
   // ---- per-lane LDS offsets (fp16 units) into an fp16 tile, swizzle folded in.
-  // K fragment of k-step ks (global 0..35): key row l32, logical chunk 2ks + h stored at
-  // chunk (2ks + h) ^ v, v = (l32 / 4) & 3; ks parity decides the sign of the v/2 term.
+  // K fragment of k-step ks (0..35): key row l32, logical chunk 2ks + h stored at chunk
+  // (2ks + h) ^ v, v = (l32 / 4) & 3; ks parity decides the sign of the v/2 term.
   const int vk = (l32 >> 2) & 3;
-  const int k_even = l32 * kKS + 8 * (h ^ (vk & 1)) + 16 * (vk >> 1);
-  const int k_odd = l32 * kKS + 8 * (h ^ (vk & 1)) - 16 * (vk >> 1);
+  int k_even = l32 * kKS + 8 * (h ^ (vk & 1)) + 16 * (vk >> 1);
+  int k_odd = l32 * kKS + 8 * (h ^ (vk & 1)) - 16 * (vk >> 1);
+  if ((kQW * half) & 1) {   // this wave's first k-step is odd: swap the two bases
+    const int t = k_even; k_even = k_odd; k_odd = t;
+  }
   // V^T fragments of k-step kk and output tile mt: rows 16kk + 4h + n/4 (first read) and
   // 8 rows further (second), logical chunk 4mt + 2(g%2) + (n%4)/2, fp16 offset 4(n&1).
   const int g = lane >> 4, n = lane & 15;
@@ -257,65 +329,86 @@ __global__ __launch_bounds__(NP * 128, 1) void mla_kernel(MlaDecodeArgs da, Spar
   const int v_lo = vrow * kKS + 8 * (vsub ^ h) + 4 * (n & 1);
   const int v_hi = (vrow + 8) * kKS + 8 * (vsub ^ ((h + 2) & 3)) + 4 * (n & 1);
 
-  f32x16 acc[kMH];
+  f32x16 acc[kMW];
 #pragma unroll
-  for (int mt = 0; mt < kMH; ++mt)
+  for (int mt = 0; mt < kMW; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  f32x4* x_own = xs + wave * 256 + lane;
-  const f32x4* x_pair = xs + (wave & ~1) * 256 + lane;   // half 0's partial, then half 1's
+  f32x4* x_own = xs + (SPLIT > 1 ? wave * 256 + lane : 0);
+  const f32x4* x_pair = xs + (SPLIT > 1 ? (wave - half) * 256 + lane : 0);   // share 0's partial
 
-  // ---- stage 3, first half: partial S^T over this wave's 288 dims, published to the peer
-  auto qk_partial = [&](auto P) -> void {
+  // Other half of the wave (lane ^ 32) without an LDS round trip.
+  auto other_half = [](float v) -> float {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
+  };
+
+  // ---- stage 3a: S^T[32 keys x 32 rows] over this wave's share of the 576 dims
+  auto qk = [&](auto P) -> f32x16 {
     const uint16_t* F = fb[P];
     f32x16 s;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
-    for (int k = 0; k < kQH; ++k) {
-      const int ks = kQH * half + k;             // parity of ks equals parity of k
+    for (int k = 0; k < kQW; ++k) {
+      const int ks = kQW * half + k;             // bases swapped above when kQW * half is odd
       const uint16_t* kp = F + ((k & 1) ? k_odd : k_even) + 16 * ks;
       s = mfma32x32x16_f16(*reinterpret_cast<const u32x4*>(kp), qb[k], s);
-      if (k % 3 == 2) __builtin_amdgcn_sched_barrier(0);   // bound the read lookahead
     }
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) x_own[64 * i4] = f32x4{s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3]};
+    return s;
   };
-  // ---- stage 3, second half: full S, online softmax, O^T += V^T P^T for this wave's dims
-  auto softmax_pv = [&](auto P) {
+  // ---- stage 3b: full S, online softmax, O^T += V^T P^T for this wave's output dims
+  auto softmax_pv = [&](auto P, f32x16 s, int t, bool conv_next) {
     const uint16_t* F = fb[P];
-    // full S = half 0 + half 1, the same operation in both waves of the pair
-    f32x16 s;
+    if constexpr (SPLIT > 1) {
+      // rebuild the full S from all published shares in one fixed order -- the same
+      // operations in every wave of the group
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 a = x_pair[64 * i4], b = x_pair[256 + 64 * i4];
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 a = x_pair[64 * i4], b = x_pair[256 + 64 * i4];
+        f32x4 sum = a + b;
+        if constexpr (SPLIT == 4) sum = sum + (x_pair[512 + 64 * i4] + x_pair[768 + 64 * i4]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[4 * i4 + i] = a[i] + b[i];
+        for (int i = 0; i < 4; ++i) s[4 * i4 + i] = sum[i];
+      }
     }
-    // scale, mask, running maximum; lane holds row `row`, keys 8(i/4) + 4h + i%4
+    // scale (and mask where needed); lane holds row `row`, keys 8(i/4) + 4h + i%4.  A tile
+    // needs no mask when every key is valid and (decode) even its last key is at or below
+    // the earliest query position.
+    const bool interior = fall[P] != 0 && (SPARSE || k_begin + t * kKT + kKT - 1 <= L - T);
     float mx = -INFINITY;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int kb4 = 8 * q4 + 4 * h;
-      const int4 id = *reinterpret_cast<const int4*>(&fk[P][kb4]);
       const f32x4 ksc = *reinterpret_cast<const f32x4*>(&fks[P][kb4]);
-      const int idv[4] = {id.x, id.y, id.z, id.w};
+      if (interior) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = (idv[i] >= 0 && idv[i] <= pos) ? s[4 * q4 + i] * ksc[i] : -INFINITY;
-        s[4 * q4 + i] = v;
-        mx = fmaxf(mx, v);
+        for (int i = 0; i < 4; ++i) {
+          s[4 * q4 + i] *= ksc[i];
+          mx = fmaxf(mx, s[4 * q4 + i]);
+        }
+      } else {
+        const int4 id = *reinterpret_cast<const int4*>(&fk[P][kb4]);
+        const int idv[4] = {id.x, id.y, id.z, id.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = (idv[i] >= 0 && idv[i] <= pos) ? s[4 * q4 + i] * ksc[i] : -INFINITY;
+          s[4 * q4 + i] = v;
+          mx = fmaxf(mx, v);
+        }
       }
-      __builtin_amdgcn_sched_barrier(0);   // one group of key metadata in registers at a time
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    if (__ballot(m_new > m_run) != 0) {
+    mx = fmaxf(mx, other_half(mx));
+    // The reference maximum moves only when a row's maximum grows by more than 2^8
+    // (log2 units): probabilities stay <= 256, exact enough in fp16, and the accumulator
+    // is rescaled almost never.  Softmax does not depend on the reference.
+    if (__ballot(mx > m_run + 8.f) != 0) {
+      const float m_new = fmaxf(m_run, mx);
       const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int mt = 0; mt < kMH; ++mt) acc[mt] *= alpha;
+      for (int mt = 0; mt < kMW; ++mt) acc[mt] *= alpha;
       m_run = m_new;
     }
     // probabilities -> fp16 B operands; k-step kk holds keys 16kk + 8(j/4) + 4h + j%4
@@ -338,61 +431,81 @@ __global__ __launch_bounds__(NP * 128, 1) void mla_kernel(MlaDecodeArgs da, Spar
                      pack_f16x2(pv[4], pv[5]), pack_f16x2(pv[6], pv[7])};
     }
     l_run += rs;
+    // the next tile's upcast (independent of this P.V) in the same block as the MFMAs
+    constexpr int Q = 1 - decltype(P)::value;
+    if (conv_next) convert_chunks(Int<Q>{});
 #pragma unroll
-    for (int mt = 0; mt < kMH; ++mt) {
-      const int col = 32 * (kMH * half + mt);
+    for (int mt = 0; mt < kMW; ++mt) {
+      const int col = 32 * (kMW * half + mt);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const u32x2 lo = lds_read_tr16(F + v_lo + 16 * kk * kKS + col);
         const u32x2 hi = lds_read_tr16(F + v_hi + 16 * kk * kKS + col);
         acc[mt] = mfma32x32x16_f16(u32x4{lo.x, lo.y, hi.x, hi.y}, pb[kk], acc[mt]);
       }
-      if (mt % 2 == 1) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
+  // ---- pipeline.  Step t computes tile t from fp16 buffer t&1 and upcasts tile t+1 into
+  // the other buffer; steps alternate the parity at compile time so the compiler can tell
+  // the raw buffers apart.  Barrier 1 (step start): step t-1 is done everywhere, so fp16
+  // buffer (t+1)&1, raw buffer t&1 and the S exchange are free.  Barrier 2 (LDS only --
+  // a later DMA may stay in flight) publishes the S shares of split waves.  Each wave
+  // waits for its own share of tile t+1's DMA before the barrier that precedes the
+  // upcast; tile t+2's DMA goes out into raw buffer t&1 after that upcast's inputs are
+  // safe.
+  //   early upcast: wait, barrier 1, upcast t+1, S, issue t+2, barrier 2, softmax, P.V
+  //   late upcast:  barrier 1, S, wait, barrier 2, issue t+2, softmax, P.V with upcast t+1
   const int n_tiles = (n_keys + kKT - 1) / kKT;
-  // One pipeline step on tile t, whose fp16 tile is buffer P.  On entry tile t+1's DMA
-  // (raw buffer !P) is in flight and raw buffer P is free.  Steps alternate P at compile
-  // time so the compiler can tell the raw buffers apart.
+  auto publish = [&](const f32x16& s) {
+    if constexpr (SPLIT > 1) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) x_own[64 * i4] = f32x4{s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3]};
+    }
+  };
   auto step = [&](auto P, int t) {
     constexpr int Q = 1 - decltype(P)::value;
-    const bool more2 = t + 2 < n_tiles;
-    if (more2) issue(P, t + 2);
-    qk_partial(P);
-    // tile t+1's raw bytes: this wave's DMAs done (only tile t+2's may remain) ...
-    if (more2) wait_vm<MIN_OPS>(); else wait_vm<0>();
-    __syncthreads();                                   // ... and everyone's; S partials published
-    softmax_pv(P);
-    if (t + 1 < n_tiles) convert(Int<Q>{});
-    __syncthreads();                                   // fp16 tile t+1 ready; X and buffers free
+    const bool conv = t + 1 < n_tiles;
+    if constexpr (LATE_CONV) {
+      __syncthreads();
+      const f32x16 s = qk(P);
+      publish(s);
+      wait_vm0();
+      barrier_lds();
+      if (t + 2 < n_tiles) issue(P, t + 2);
+      softmax_pv(P, s, t, conv);
+      if (conv) convert_meta(Int<Q>{});
+    } else {
+      wait_vm0();
+      __syncthreads();
+      if (conv) convert(Int<Q>{});
+      const f32x16 s = qk(P);
+      if (t + 2 < n_tiles) issue(P, t + 2);
+      publish(s);
+      if constexpr (SPLIT > 1) barrier_lds();
+      softmax_pv(P, s, t, false);
+    }
   };
-
   issue(Int<0>{}, 0);
-  if (n_tiles > 1) {
-    issue(Int<1>{}, 1);
-    wait_vm<MIN_OPS>();
-  } else {
-    wait_vm<0>();
-  }
+  wait_vm0();
   __syncthreads();
   convert(Int<0>{});
-  __syncthreads();
+  if (n_tiles > 1) issue(Int<1>{}, 1);
   for (int t = 0; t < n_tiles; t += 2) {
     step(Int<0>{}, t);
     if (t + 1 < n_tiles) step(Int<1>{}, t + 1);
   }
 
-  // ---- finish: full row sum over the two lane halves, write this wave's 256 dims
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // ---- finish: full row sum over the two lane halves, write this wave's dims
+  const float l_tot = l_run + other_half(l_run);
   if (!row_ok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse2 = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
-  // acc[mt][4q + i] = O[row][256 half + 32mt + 8q + 4h + i]
+  // acc[mt][4q + i] = O[row][32 (kMW half + mt) + 8q + 4h + i]
   if constexpr (SPARSE) {
-    uint16_t* op = sa.out + ((size_t)unit * Hq + row) * kDv + 256 * half + 4 * h;
+    uint16_t* op = sa.out + ((size_t)unit * Hq + row) * kDv + 32 * kMW * half + 4 * h;
 #pragma unroll
-    for (int mt = 0; mt < kMH; ++mt)
+    for (int mt = 0; mt < kMW; ++mt)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         u32x2 w;
@@ -404,9 +517,9 @@ __global__ __launch_bounds__(NP * 128, 1) void mla_kernel(MlaDecodeArgs da, Spar
       sa.lse[(size_t)unit * Hq + row] = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
   } else {
     const size_t pbase = ((size_t)unit * da.max_splits + unit_split) * rows_total + row;
-    float* op = da.part_o + pbase * kDv + 256 * half + 4 * h;
+    float* op = da.part_o + pbase * kDv + 32 * kMW * half + 4 * h;
 #pragma unroll
-    for (int mt = 0; mt < kMH; ++mt)
+    for (int mt = 0; mt < kMW; ++mt)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<f32x4*>(op + 32 * mt + 8 * q) =
@@ -415,24 +528,44 @@ __global__ __launch_bounds__(NP * 128, 1) void mla_kernel(MlaDecodeArgs da, Spar
   }
 }
 
-constexpr int kDecodePairs = PA_MLA_DECODE_PAIRS, kSparsePairs = 2;
+#ifndef PA_MLA_DECODE_WAVES
+#define PA_MLA_DECODE_WAVES 8
+#endif
+#ifndef PA_MLA_DECODE_SPLIT
+#define PA_MLA_DECODE_SPLIT 2
+#endif
+constexpr int kDecodeWaves = PA_MLA_DECODE_WAVES, kDecodeSplit = PA_MLA_DECODE_SPLIT;
+#ifndef PA_MLA_SPARSE_WAVES
+#define PA_MLA_SPARSE_WAVES 4
+#endif
+#ifndef PA_MLA_SPARSE_SPLIT
+#define PA_MLA_SPARSE_SPLIT 2
+#endif
+constexpr int kSparseWaves = PA_MLA_SPARSE_WAVES, kSparseSplit = PA_MLA_SPARSE_SPLIT;
+constexpr int kDecodeRows = 32 * kDecodeWaves / kDecodeSplit, kSparseRows = 32 * kSparseWaves / kSparseSplit;
 
 }  // namespace
 
 hipError_t launch_mla_decode(const MlaDecodeArgs& a, hipStream_t stream) {
   const int rows = a.q_per_seq * a.num_q_heads;
-  const unsigned grid = (unsigned)a.num_seqs * a.max_splits * ((rows + 32 * kDecodePairs - 1) / (32 * kDecodePairs));
+  const unsigned grid = (unsigned)a.num_seqs * a.max_splits * ((rows + kDecodeRows - 1) / kDecodeRows);
   if (grid == 0) return hipSuccess;
   SparseMlaArgs none{};
-  hipLaunchKernelGGL((mla_kernel<false, kDecodePairs>), dim3(grid), dim3(128 * kDecodePairs), 0, stream, a, none);
+  hipLaunchKernelGGL((mla_kernel<false, kDecodeWaves, kDecodeSplit, true, false>), dim3(grid), dim3(64 * kDecodeWaves), 0,
+                     stream, a, none);
   return hipGetLastError();
 }
 
 hipError_t launch_sparse_mla(const SparseMlaArgs& a, hipStream_t stream) {
-  const unsigned grid = (unsigned)a.n_q * ((a.num_q_heads + 32 * kSparsePairs - 1) / (32 * kSparsePairs));
+  const unsigned grid = (unsigned)a.n_q * ((a.num_q_heads + kSparseRows - 1) / kSparseRows);
   if (grid == 0) return hipSuccess;
   MlaDecodeArgs none{};
-  hipLaunchKernelGGL((mla_kernel<true, kSparsePairs>), dim3(grid), dim3(128 * kSparsePairs), 0, stream, none, a);
+  if (a.k <= kSelLds && a.bt_stride <= kBtLds)
+    hipLaunchKernelGGL((mla_kernel<true, kSparseWaves, kSparseSplit, true, true>), dim3(grid), dim3(64 * kSparseWaves), 0,
+                       stream, none, a);
+  else
+    hipLaunchKernelGGL((mla_kernel<true, kSparseWaves, kSparseSplit, false, true>), dim3(grid), dim3(64 * kSparseWaves), 0,
+                       stream, none, a);
   return hipGetLastError();
 }
 
