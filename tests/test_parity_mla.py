@@ -100,6 +100,23 @@ def test_topk_hook_random_scores(pa_lib):
         assert np.array_equal(got[r], oracle.topk_indices(scores[r].astype(np.float64), valid[r], 2048)), r
 
 
+def test_topk_hook_long_and_clustered_rows(pa_lib):
+    """Rows beyond the LDS bitmap (300,000 tokens) and rows whose scores crowd one
+    histogram bin (all within a factor 1.001) take the multi-pass path; both must match."""
+    import torch
+    rng = np.random.default_rng(6)
+    n = 300_000
+    scores = np.empty((3, n), np.float32)
+    scores[0] = rng.standard_normal(n)
+    scores[1] = 1.0 + 1e-3 * rng.random(n)               # one 12-bit key bin holds everything
+    scores[2] = rng.standard_normal(n)
+    valid = np.array([n, 200_000, 150_000], np.int32)
+    got = pa_lib.pa_test_topk_from_scores(torch.from_numpy(scores).cuda(), torch.from_numpy(valid).cuda(),
+                                          2048).cpu().numpy()
+    for r in range(3):
+        assert np.array_equal(got[r], oracle.topk_indices(scores[r].astype(np.float64), valid[r], 2048)), r
+
+
 def _indexer(pa, dev, k):
     import torch
     n_q = dev.q_idx.shape[0]
