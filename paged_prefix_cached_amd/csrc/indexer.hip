@@ -8,8 +8,9 @@
 //
 // A workgroup of 8 waves owns 8 query rows (one per wave) and a chunk of keys.  Key
 // tiles of 64 tokens are gathered through the block table, upcast exactly from FP8 to
-// bf16 and staged in LDS once for all 8 queries.  Each wave keeps its query's 64 x 128
-// bf16 heads in registers (A operand) and computes C[heads x keys] with
+// bf16 and staged in LDS once for all 8 queries (two buffers; the following tile's bytes
+// are in registers meanwhile).  Each wave keeps its query's 64 x 128 bf16 heads in
+// registers (A operand) and computes C[heads x keys] with
 // v_mfma_f32_16x16x32_bf16: in the C layout a lane holds 4 heads of one key, so the
 // weighted ReLU head sum is 16 fused multiply-adds in registers plus a 2-step reduction
 // across the 4 lane groups.
@@ -36,8 +37,8 @@ __device__ __forceinline__ int find_seq(const int32_t* q_start, int num_seqs, in
 
 template <int NHT>   // head tiles of 16 (num_heads / 16)
 __global__ __launch_bounds__(512) void indexer_kernel(IndexerArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_s[kKT * kKStride];
-  __shared__ float sc_s[kKT];
+  __shared__ __attribute__((aligned(16))) uint16_t k_s[2][kKT * kKStride];
+  __shared__ float sc_s[2][kKT];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m16 = lane & 15, grp = lane >> 4;
   const int n_chunks = (a.max_total_len + kChunk - 1) / kChunk;
@@ -86,48 +87,67 @@ __global__ __launch_bounds__(512) void indexer_kernel(IndexerArgs a) {
     }
     float* srow = mine ? a.scores + (size_t)i * a.score_stride : nullptr;
     const int kc_end = min(c1, blk_max_pos + 1);
-    for (int kb = c0; kb < kc_end; kb += kKT) {
-      __syncthreads();
-      // gather + upcast 64 keys: 64 x 128 B = 512 chunks of 16 B, one per thread
-      {
-        const int key = tid >> 3, dc = tid & 7;
-        const int t = kb + key;
-        const int pb = t < total ? phys_block(bt_row, t / kBs, n_lblocks, a.num_blocks) : -1;
-        u32x4 raw = pb >= 0 ? ld16(a.keys + ((size_t)pb * kBs + t % kBs) * kD + 16 * dc) : u32x4{0, 0, 0, 0};
-        uint32_t bf[8];
+    // Tile pipeline, one barrier per tile: at the top of step t the FP8 bytes of tile t+1
+    // (loaded during step t-1) are upcast into LDS buffer (t+1)&1, which the barrier
+    // ending step t-1 freed; tile t+2's loads go out; tile t is computed from buffer t&1.
+    const int key = tid >> 3, dc = tid & 7;        // 64 keys x 128 B: one 16 B chunk a thread
+    u32x4 raw = {0, 0, 0, 0};
+    float rsc = 0.f;
+    auto load_tile = [&](int kb) {
+      const int t = kb + key;
+      const int pb = t < total ? phys_block(bt_row, t / kBs, n_lblocks, a.num_blocks) : -1;
+      raw = pb >= 0 ? ld16(a.keys + ((size_t)pb * kBs + t % kBs) * kD + 16 * dc) : u32x4{0, 0, 0, 0};
+      if (dc == 0) rsc = pb >= 0 ? a.key_scale[(size_t)pb * kBs + t % kBs] : 0.f;
+    };
+    auto store_tile = [&](int buf) {
+      uint32_t bf[8];
 #pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4) {
-          const u32x2 c = fp8x4_to_bf16x4(raw[w4]);
-          bf[2 * w4] = c.x;
-          bf[2 * w4 + 1] = c.y;
+      for (int w4 = 0; w4 < 4; ++w4) {
+        const u32x2 c = fp8x4_to_bf16x4(raw[w4]);
+        bf[2 * w4] = c.x;
+        bf[2 * w4 + 1] = c.y;
+      }
+      uint16_t* kp = k_s[buf] + key * kKStride + 16 * dc;
+      st16(kp, u32x4{bf[0], bf[1], bf[2], bf[3]});
+      st16(kp + 8, u32x4{bf[4], bf[5], bf[6], bf[7]});
+      if (dc == 0) sc_s[buf][key] = rsc;
+    };
+    if (c0 < kc_end) {
+      __syncthreads();                               // a previous sequence pass is done with LDS
+      load_tile(c0);
+      store_tile(0);
+      if (c0 + kKT < kc_end) load_tile(c0 + kKT);
+      __syncthreads();
+    }
+    for (int kb = c0, tt = 0; kb < kc_end; kb += kKT, ++tt) {
+      const int buf = tt & 1;
+      if (kb + kKT < kc_end) {
+        store_tile(buf ^ 1);                         // tile tt+1 (its loads went out last step)
+        if (kb + 2 * kKT < kc_end) load_tile(kb + 2 * kKT);
+      }
+      if (mine && kb <= pos) {
+#pragma unroll
+        for (int st = 0; st < kKT / 16; ++st) {
+          u32x4 kb4[4];
+          const uint16_t* kp = k_s[buf] + (16 * st + m16) * kKStride + 8 * grp;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) kb4[ks] = *reinterpret_cast<const u32x4*>(kp + 32 * ks);
+          float part = 0.f;
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht) {
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) c = mfma16x16x32(qa[ht][ks], kb4[ks], c);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) part = fmaf(wv[ht][r], fmaxf(c[r], 0.f), part);
+          }
+          part += __shfl_xor(part, 16);
+          part += __shfl_xor(part, 32);
+          const int t = kb + 16 * st + m16;
+          if (grp == 0 && t <= pos && t < c1) srow[t] = part * sc_s[buf][16 * st + m16] + 0.f;
         }
-        uint16_t* kp = k_s + key * kKStride + 16 * dc;
-        st16(kp, u32x4{bf[0], bf[1], bf[2], bf[3]});
-        st16(kp + 8, u32x4{bf[4], bf[5], bf[6], bf[7]});
-        if (dc == 0) sc_s[key] = pb >= 0 ? a.key_scale[(size_t)pb * kBs + t % kBs] : 0.f;
       }
       __syncthreads();
-      if (!mine || kb > pos) continue;
-#pragma unroll
-      for (int st = 0; st < kKT / 16; ++st) {
-        u32x4 kb4[4];
-        const uint16_t* kp = k_s + (16 * st + m16) * kKStride + 8 * grp;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kb4[ks] = *reinterpret_cast<const u32x4*>(kp + 32 * ks);
-        float part = 0.f;
-#pragma unroll
-        for (int ht = 0; ht < NHT; ++ht) {
-          f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) c = mfma16x16x32(qa[ht][ks], kb4[ks], c);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) part = fmaf(wv[ht][r], fmaxf(c[r], 0.f), part);
-        }
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 32);
-        const int t = kb + 16 * st + m16;
-        if (grp == 0 && t <= pos && t < c1) srow[t] = part * sc_s[16 * st + m16] + 0.f;
-      }
     }
     // keys of this chunk past the row's position: -inf (the tile loop wrote t <= pos)
     if (mine) {
