@@ -35,6 +35,8 @@ METRIC = "paged attn: decode KV GB/s, prefill TFLOP/s, tokens/s; % HBM/MFMA roof
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 FP8_PEAK_TFLOPS = 5000.0
+DECODE_SOURCES = ["paged_prefix_cached_amd/csrc/decode_gqa.hip", "paged_prefix_cached_amd/csrc/pa_device.h",
+                  "paged_prefix_cached_amd/csrc/pa_internal.h"]
 
 
 def log(*a):
@@ -67,6 +69,28 @@ def timed_steps(step, steps, warmup, kernel=None):
         per_kernel.setdefault(name, []).append(ms)
     avg = {k: float(np.mean(v)) for k, v in per_kernel.items()}
     return (t1 - t0) * 1e3 / steps, avg
+
+
+def measured_traffic(counters_file: str, sources: list[str]):
+    """HBM bytes per launch from a committed rocprofv3 counter summary (FETCH_SIZE and
+    WRITE_SIZE, scaled by a copy-kernel calibration), or None when the summary is absent
+    or was taken on different kernel sources (sha256 over `sources`)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", counters_file)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for src in sources:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if fields.get("source_sha256") != h.hexdigest():
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 # --------------------------------------------------------------------------- decode (headline)
@@ -119,7 +143,9 @@ def bench_decode(args, dev_name, share=True):
         "kernel_ms": kern,
         "roofline": {"bound": "hbm", "achieved": algo / (k_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": algo / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "traffic": None, "kernel": "gqa_decode_kernel",
+                     "traffic": measured_traffic("gqa_decode_kernel.hbm-counters.decode-64seq.txt", DECODE_SOURCES)
+                     if share else None,
+                     "kernel": "gqa_decode_kernel",
                      "bytes_per_launch": algo,
                      "per_unit": "4096 B per distinct cached token (8 KV heads x 128 x K,V x bf16) + q,out"},
         "config": {"workload": "paged GQA decode: 64 seqs x 1 query token, 32q/8kv heads, d128, bf16, "
