@@ -7,17 +7,23 @@
 // A workgroup owns 128 query rows of one (sequence, KV head): 128/G new tokens x the G
 // query heads that read that KV head, so every K/V tile staged in LDS serves all heads
 // of the group.  Four waves own 32 rows each.  The key loop walks the sequence's block
-// table in 64-key tiles (four 16-token blocks):
-//   * the whole workgroup loads the next tile from HBM into registers while the current
-//     one is computed (coalesced 16-byte loads; a (block, head) tile is contiguous);
-//   * K goes to LDS row-major (padded rows) as bf16; V goes to LDS transposed (dims x
-//     keys) as fp16 (exact conversion), transposed in registers 4 keys x 8 dims at a
-//     time; V rows past the sequence end are stored as zeros;
+// table in 64-key tiles (four 16-token blocks), one barrier per tile:
+//   * at the top of step t, tile t+1 (loaded into registers during step t-1, coalesced
+//     16-byte loads of contiguous (block, head) tiles) is stored into the other LDS
+//     buffer -- K row-major as bf16, V row-major as fp16 (exact conversion), V rows past
+//     the sequence end as zeros -- and tile t+2's loads go out;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: Q^T stays in registers for the whole
-//     loop; in the C layout each lane holds one query row, so the online softmax needs
-//     a single cross-lane step and the probabilities (rounded to fp16, which keeps 11
-//     significant bits) feed O^T += V^T P^T (v_mfma_f32_32x32x16_f16) directly as the B
-//     operand, in the same register order as the V^T fragments read from LDS.
+//     loop; in the C layout each lane holds one query row, so the online softmax needs a
+//     single cross-lane step.  The softmax scale is fused into the exponent
+//     (p = 2^(s c - m), max taken on raw scores), and the reference maximum moves only
+//     when a row's maximum grows by more than 2^8 (log2 units): probabilities up to 256
+//     stay exact enough in fp16, and the accumulator is almost never rescaled;
+//   * O^T += V^T P^T with v_mfma_f32_32x32x16_f16: P (fp16, 11 significant bits) comes
+//     straight from registers, V^T fragments from ds_read_b64_tr_b16 transpose reads of
+//     the row-major V tile (the reduction index relabelled to match the C layout).
+// Row strides: K 272 B (68 dwords: the 16 rows of a b128 read phase hit distinct banks),
+// V (D + 32) fp16 (D/2 + 16 dwords, 16 or 48 mod 64: the 4 rows of a transpose read
+// phase hit distinct banks).
 // Workgroups of the same (sequence, KV head) are mapped onto one XCD so its L2 serves
 // the shared prefix to all of them.
 #include "pa_device.h"
@@ -33,21 +39,21 @@ constexpr int kKT = 64;                   // keys per tile
 
 template <int D>
 struct PrefillSmem {
-  static constexpr int kStride = D + 8;        // K rows (bf16): 16-byte pad
-  static constexpr int vtStride = kKT + 8;     // V^T rows (bf16)
-  uint16_t k[kKT * kStride];
-  uint16_t vt[D * vtStride];
+  static constexpr int kStride = D + 8;        // K rows (bf16)
+  static constexpr int vStride = D + 32;       // V rows (fp16)
+  uint16_t k[2][kKT * kStride];
+  uint16_t v[2][kKT * vStride];
 };
 
 template <int D, int G>
 __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs a) {
   constexpr int KS = D / 16;          // QK k-steps (32x32x16)
   constexpr int MT = D / 32;          // O^T tiles of 32 dims
-  constexpr int KCH = kKT * D / 8;    // 16-byte K chunks per tile
-  constexpr int KPT = KCH / kThreads; // K chunks per thread
-  constexpr int VGR = (kKT / 4) * (D / 8);  // (4 keys x 8 dims) V groups per tile
+  constexpr int KCH = kKT * D / 8;    // 16-byte chunks per K (or V) tile
+  constexpr int KPT = KCH / kThreads; // chunks per thread
   constexpr int TT = kRows / G;       // new tokens per workgroup
   using Sm = PrefillSmem<D>;
+  static_assert(KCH % kThreads == 0, "whole chunks per thread");
   __shared__ __attribute__((aligned(16))) Sm sm;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -85,140 +91,139 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
   const int kv_end = min(cached + last_tok_wg + 1, total);
   const int wave_min_pos = cached + min(tok0 + (wave * kRowsPerWave) / G, nl - 1);
   const int wave_max_pos = min(cached + min(tok0 + (wave * kRowsPerWave + kRowsPerWave - 1) / G, nl - 1), total - 1);
+  const float c = a.scale_log2;
 
   f32x16 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;   // m_run in scaled log2 units
 
-  // ---- register prefetch of one K/V tile
-  u32x4 kreg[KPT];
-  u32x4 vreg[4];
-  auto load_tile = [&](int kt) {
+  // ---- register prefetch of one K/V tile: chunk ci = tid + 256 i holds 8 dims of one key.
+  // A tile's four block ids are looked up first (same addresses in every lane); the K/V
+  // loads go out together once they are back, so a tile costs one table round trip, not
+  // one per chunk (vector-memory counters complete in order).
+  u32x4 kreg[KPT], vreg[KPT];
+  int pbs[kKT / 16];
+  auto lookup_blocks = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < kKT / 16; ++j) pbs[j] = phys_block(bt_row, (kt >> 4) + j, n_lblocks, a.num_blocks);
+  };
+  auto load_kv = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int c = tid + kThreads * i;
-      const int key = c / (D / 8), dc = c % (D / 8);
-      const int pb = phys_block(bt_row, (kt + key) >> 4, n_lblocks, a.num_blocks);
-      kreg[i] = pb >= 0 ? ld16(a.k + ((size_t)pb * Hkv + g) * head_stride + (size_t)(key & 15) * D + 8 * dc)
-                        : u32x4{0, 0, 0, 0};
-    }
-    if (tid < VGR) {
-      const int kg = tid % (kKT / 4), dc = tid / (kKT / 4);
-      const int pb = phys_block(bt_row, (kt + 4 * kg) >> 4, n_lblocks, a.num_blocks);
-      if (pb >= 0) {
-        const uint16_t* vp = a.v + ((size_t)pb * Hkv + g) * head_stride + (size_t)((4 * kg) & 15) * D + 8 * dc;
+      const int ci = tid + kThreads * i;
+      const int key = ci / (D / 8), dc = ci % (D / 8);
+      int pb = pbs[0];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          vreg[e] = (kt + 4 * kg + e < total) ? ld16(vp + (size_t)e * D) : u32x4{0, 0, 0, 0};
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vreg[e] = u32x4{0, 0, 0, 0};
-      }
+      for (int j = 1; j < kKT / 16; ++j) pb = (key >> 4) == j ? pbs[j] : pb;
+      const size_t off = ((size_t)pb * Hkv + g) * head_stride + (size_t)(key & 15) * D + 8 * dc;
+      kreg[i] = pb >= 0 ? ld16(a.k + off) : u32x4{0, 0, 0, 0};
+      vreg[i] = (pb >= 0 && kt + key < total) ? ld16(a.v + off) : u32x4{0, 0, 0, 0};
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int c = tid + kThreads * i;
-      const int key = c / (D / 8), dc = c % (D / 8);
-      st16(sm.k + key * Sm::kStride + 8 * dc, kreg[i]);
-    }
-    if (tid < VGR) {
-      const int kg = tid % (kKT / 4), dc = tid / (kKT / 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) vreg[e][w] = bf16x2_to_f16x2(vreg[e][w]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        u32x2 lo, hi;
-        lo.x = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
-        lo.y = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u);
-        hi.x = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
-        hi.y = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u);
-        *reinterpret_cast<u32x2*>(sm.vt + (8 * dc + 2 * w) * Sm::vtStride + 4 * kg) = lo;
-        *reinterpret_cast<u32x2*>(sm.vt + (8 * dc + 2 * w + 1) * Sm::vtStride + 4 * kg) = hi;
-      }
+      const int ci = tid + kThreads * i;
+      const int key = ci / (D / 8), dc = ci % (D / 8);
+      st16(sm.k[buf] + key * Sm::kStride + 8 * dc, kreg[i]);
+      const u32x4 v16 = {bf16x2_to_f16x2(vreg[i].x), bf16x2_to_f16x2(vreg[i].y),
+                         bf16x2_to_f16x2(vreg[i].z), bf16x2_to_f16x2(vreg[i].w)};
+      st16(sm.v[buf] + key * Sm::vStride + 8 * dc, v16);
     }
   };
 
-  load_tile(0);
-  for (int kt = 0; kt < kv_end; kt += kKT) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (kt + kKT < kv_end) load_tile(kt + kKT);
-    if (kt > wave_max_pos) continue;   // this wave's rows see none of these keys
+  // V^T fragment offsets (fp16 units): first read rows 16 kk + 4 h + n/4 of a 32-key
+  // sub-tile, dims 32 mt + 16 (g16 & 1) + 4 (n & 3); second read 8 rows further.
+  const int g16 = lane >> 4, n16 = lane & 15;
+  const int v_lo = (4 * h32 + (n16 >> 2)) * Sm::vStride + 16 * (g16 & 1) + 4 * (n16 & 3);
+
+  auto compute = [&](int buf, int kt) {
+    const uint16_t* kt_s = sm.k[buf];
+    const uint16_t* vt_s = sm.v[buf];
     // ---- S^T = K Q^T, two 32-key sub-tiles
     f32x16 sacc[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[st][i] = 0.f;
-      const uint16_t* kp = sm.k + (32 * st + c32) * Sm::kStride + 8 * h32;
+      const uint16_t* kp = kt_s + (32 * st + c32) * Sm::kStride + 8 * h32;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         sacc[st] = mfma32x32x16(*reinterpret_cast<const u32x4*>(kp + 16 * ks), qb[ks], sacc[st]);
     }
-    // ---- scale, causal mask, online softmax (log2 domain)
+    // ---- causal mask (diagonal tiles only) and the row maximum on raw scores
     const bool need_mask = kt + kKT - 1 > wave_min_pos;
     float mx = -INFINITY;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float v = sacc[st][i] * a.scale_log2;
         if (need_mask) {
           const int key = kt + 32 * st + 8 * (i >> 2) + 4 * h32 + (i & 3);
-          v = key <= pos ? v : -INFINITY;
+          if (key > pos) sacc[st][i] = -INFINITY;
         }
-        sacc[st][i] = v;
-        mx = fmaxf(mx, v);
+        mx = fmaxf(mx, sacc[st][i]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    float alpha = 1.f, rs = 0.f;
-    if (m_new != -INFINITY) {
-      alpha = fast_exp2(m_run - m_new);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+    if (__ballot(mx > m_run + 8.f) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;   // fully masked rows: p = 0
+    float rs = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(sacc[st][i] - m_new);
-          sacc[st][i] = p;
-          rs += p;
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(sacc[st][i], c, neg_m));
+        sacc[st][i] = p;
+        rs += p;
+      }
+    l_run += rs;
+    // ---- O^T += V^T P^T: k-step (st, kk) holds keys 32 st + 16 kk + 8 (j/4) + 4 h + j%4
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int r0 = 8 * kk;
+        const u32x4 pb = {pack_f16x2(sacc[st][r0 + 0], sacc[st][r0 + 1]), pack_f16x2(sacc[st][r0 + 2], sacc[st][r0 + 3]),
+                          pack_f16x2(sacc[st][r0 + 4], sacc[st][r0 + 5]), pack_f16x2(sacc[st][r0 + 6], sacc[st][r0 + 7])};
+        const uint16_t* vp = vt_s + (32 * st + 16 * kk) * Sm::vStride + v_lo;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const u32x2 lo = lds_read_tr16(vp + 32 * mt);
+          const u32x2 hi = lds_read_tr16(vp + 8 * Sm::vStride + 32 * mt);
+          acc[mt] = mfma32x32x16_f16(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, acc[mt]);
         }
-    } else {
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[st][i] = 0.f;
-    }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
-    // ---- O^T += V^T P^T, four 16-key k-steps
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int st = ks >> 1, r0 = 8 * (ks & 1);
-      u32x4 pb;
-      pb.x = pack_f16x2(sacc[st][r0 + 0], sacc[st][r0 + 1]);
-      pb.y = pack_f16x2(sacc[st][r0 + 2], sacc[st][r0 + 3]);
-      pb.z = pack_f16x2(sacc[st][r0 + 4], sacc[st][r0 + 5]);
-      pb.w = pack_f16x2(sacc[st][r0 + 6], sacc[st][r0 + 7]);
-      const int kbase = 32 * st + 16 * (ks & 1) + 4 * h32;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint16_t* vp = sm.vt + (32 * mt + c32) * Sm::vtStride + kbase;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
-        acc[mt] = mfma32x32x16_f16(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, acc[mt]);
       }
+  };
+
+  // ---- pipeline: one barrier per tile; buffer t&1 holds tile t
+  lookup_blocks(0);
+  load_kv(0);
+  store_tile(0);
+  if (kKT < kv_end) {
+    lookup_blocks(kKT);
+    load_kv(kKT);
+  }
+  __syncthreads();
+  for (int kt = 0, t = 0; kt < kv_end; kt += kKT, ++t) {
+    const int buf = t & 1;
+    if (kt + kKT < kv_end) {
+      const bool more = kt + 2 * kKT < kv_end;
+      if (more) lookup_blocks(kt + 2 * kKT);     // in flight while tile t+1 is stored
+      store_tile(buf ^ 1);                       // tile t+1, read last in step t-1
+      if (more) load_kv(kt + 2 * kKT);
     }
+    if (kt <= wave_max_pos) compute(buf, kt);    // else this wave's rows see none of these keys
+    __syncthreads();
   }
 
   // ---- normalise and write
