@@ -1,5 +1,5 @@
 // Paged GQA decode (bf16 K/V, block size 16) that reads every distinct KV block once per
-// group of sequences, with split-K over the context and a fixed-order combine.
+// group of sequences and spreads the work evenly over the GPU.
 //
 // Sources: vLLM AgentX article (news.ainew.jp), "Re-evaluating agentic workloads" (>96 %
 // prefix-cache hits; sub-agents fork from the parent context, so sequences in flight share
@@ -7,55 +7,202 @@
 // the same physical blocks, Figure 4) and "Kimi K3" (partial outputs and their
 // log-sum-exp merged with online softmax, Figure 7).
 //
-// Work unit = (group of consecutive sequences, KV head g, split j).  A group holds
-// M = 32 / (T*G) sequences, so its T query tokens x G heads per sequence fill the 32 rows
-// of a v_mfma_f32_32x32x16 tile (cfg: 8 sequences x 4 heads).  For each 32-key tile of the
-// split (two 16-token blocks) the wave looks up every member's pair of physical blocks and
-// processes each DISTINCT pair once, for all member rows that reference it (ballot +
-// readlane, no LDS): blocks shared by forked sequences are fetched from HBM once instead of
-// once per sequence.  Correctness never depends on the grouping; a batch whose sessions
-// are not adjacent just shares less.
-//
-// Per processed pair a wave:
-//   * has issued the pair's K and V loads while the previous pair was being computed
-//     (register double buffering: one pass always in flight per wave);
-//   * uses K straight from registers as the A operand of S^T = K Q^T (lane l: key l%32);
-//     Q^T fragments come from LDS, staged once per workgroup (B operand, lane = query row);
-//   * masks rows that do not reference the pair and keys past each row's position, then
-//     updates its online softmax in-lane (one xor-32 step per row);
-//   * writes V (bf16; rows past the pair's longest member zeroed) row-major into its LDS
-//     slice and accumulates O^T += V^T P^T with two v_mfma_f32_32x32x16_bf16, P split
-//     into bf16 hi + lo parts (P keeps ~16 significant bits: rounding P to one bf16 would
-//     cost ~1.5e-3 relative error in O); the V^T fragments come from
-//     ds_read_b64_tr_b16 transpose reads, P straight from registers.
-// The accumulator is rescaled only when a row's running maximum grows, which after the
-// first tiles of a long context is rare.
-// The 4 waves of a workgroup take tiles w, w+4, ... of the split; their states are merged
-// pairwise through LDS in a fixed order, and the split's normalised partial output plus
-// its log2-sum-exp go to the workspace.  combine_kernel merges splits in order.
+// A group holds M = 32 / (T*G) consecutive sequences, so its T query tokens x G heads per
+// sequence fill the 32 rows of a v_mfma_f32_32x32x16 tile (8 sequences x 4 heads for
+// 32q/8kv heads and one token).  Four launches:
+//   1. decode_plan_kernel lists, for every group and 32-key tile (two 16-token blocks),
+//      the DISTINCT block pairs its members reference, each with the set of members that
+//      share it and the number of its keys that hold data.  Blocks that forked sequences
+//      share become one pass for all of them: fetched from HBM once, not once per member.
+//   2. decode_units_kernel cuts each group's pass list into units of at most kUnitPasses
+//      passes, numbers them and resets the work queue.  A unit's length is fixed by its
+//      passes, not by its keys, so units where members diverge (one pass per member per
+//      tile) cost the same as units over a shared prefix.
+//   3. gqa_decode_kernel: a persistent grid whose workgroups take (unit, KV head) items
+//      from an atomic queue until it is empty.  The four waves of a workgroup take the
+//      unit's passes round robin; per pass a wave
+//        * has issued the pass's K and V loads while the previous pass was computed
+//          (register double buffering: one pass always in flight per wave);
+//        * uses K straight from registers as the A operand of S^T = K Q^T (lane l: key
+//          l%32); Q^T fragments come from LDS (B operand, lane = query row);
+//        * masks rows whose member does not share the pass and keys past each row's
+//          position, then updates its online softmax in-lane (one xor-32 step per row);
+//        * writes V (bf16; keys without data zeroed) row-major into its LDS slice and
+//          accumulates O^T += V^T P^T with two v_mfma_f32_32x32x16_bf16, P split into bf16
+//          hi + lo parts (P keeps ~16 significant bits: one bf16 would cost ~1.5e-3
+//          relative error in O); the V^T fragments come from ds_read_b64_tr_b16
+//          transpose reads, P straight from registers.
+//      The accumulator is rescaled only when a row's running maximum grows.  The wave
+//      states are merged pairwise through LDS in a fixed order and the unit's normalised
+//      partial output and log2-sum-exp go to the workspace.
+//   4. combine_kernel merges each row's unit partials in unit order.
+// Every partition depends on the inputs only, so results are identical run to run.
+#include <algorithm>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
+
+GqaDecodeDims gqa_decode_dims(int num_seqs, int q_per_seq, int num_q_heads, int num_kv_heads,
+                              int max_context_len) {
+  GqaDecodeDims d{};
+  const int R = q_per_seq * (num_q_heads / num_kv_heads);
+  d.members = R >= 32 ? 1 : 32 / R;
+  d.n_groups = (num_seqs + d.members - 1) / d.members;
+  const long n_tiles = (max_context_len + 31) / 32;
+  d.n_chunks = (int)((n_tiles + kPlanTiles - 1) / kPlanTiles);
+  d.region_cap = kPlanTiles * d.members;
+  // a member references at most one distinct pair per tile of its context
+  const long regions = (long)d.n_groups * d.n_chunks;
+  d.units_cap = (int)(((long)num_seqs * n_tiles + kUnitPasses - 1) / kUnitPasses + regions);
+  return d;
+}
+
 namespace {
 
 constexpr int kWaves = 4;
 constexpr int kTile = 32;               // keys per pass (two 16-token blocks)
 
+// ---------------------------------------------------------------------------------
+// 1. Plan: one workgroup per (group, chunk of kPlanTiles tiles), one thread per tile.
+// Member m takes part in tile t iff 32t < L_m; its pair is (block 2t, block 2t+1), each
+// -1 when past its blocks or out of range (read as zeros).  Pairs are deduplicated in
+// member order; a pass lists the members sharing its pair and how many of its 32 keys
+// hold data for the longest of them.
+__global__ __launch_bounds__(256) void decode_plan_kernel(GqaDecodeArgs a) {
+  __shared__ int2 pr[32][kPlanTiles];
+  __shared__ int len_s[32];
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int M = a.dims.members, region = blockIdx.x;
+  const int g = region / a.dims.n_chunks, c = region % a.dims.n_chunks;
+  const int s0 = g * M;
+  if (tid < 32) {
+    int L = 0;
+    if (tid < M && s0 + tid < a.num_seqs) L = min(max(a.context_len[s0 + tid], 0), a.max_context_len);
+    len_s[tid] = L;
+  }
+  __syncthreads();
+  const int tile = c * kPlanTiles + tid, kb = tile * kTile;
+  uint32_t part = 0;                    // members taking part in this tile
+  for (int mm = 0; mm < M; ++mm) {
+    const int L = len_s[mm];
+    int2 p = {-1, -1};
+    if (kb < L) {
+      const int nlb = (L + 15) >> 4;
+      const int32_t* row = a.bt + (size_t)(s0 + mm) * a.bt_stride;
+      p.x = phys_block(row, 2 * tile, nlb, a.num_blocks);
+      p.y = phys_block(row, 2 * tile + 1, nlb, a.num_blocks);
+      part |= 1u << mm;
+    }
+    pr[mm][tid] = p;
+  }
+  // first occurrences of each distinct pair (a column of pr is this thread's alone)
+  uint32_t first = 0;
+  for (int mm = 0; mm < M; ++mm) {
+    if (!((part >> mm) & 1)) continue;
+    const int2 p = pr[mm][tid];
+    bool is_first = true;
+    for (int m2 = 0; m2 < mm; ++m2) {
+      const int2 q2 = pr[m2][tid];
+      if (((part >> m2) & 1) && q2.x == p.x && q2.y == p.y) { is_first = false; break; }
+    }
+    if (is_first) first |= 1u << mm;
+  }
+  const int cnt = __builtin_popcount(first);
+  // exclusive scan of cnt over the workgroup
+  int x = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int off = x - cnt, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    off += w < wave ? wsum[w] : 0;
+    total += wsum[w];
+  }
+  if (tid == 0) a.n_passes[region] = total;
+  uint32_t* out = a.passes + ((size_t)region * a.dims.region_cap + off) * 4;
+  for (int mm = 0; mm < M; ++mm) {
+    if (!((first >> mm) & 1)) continue;
+    const int2 p = pr[mm][tid];
+    uint32_t mask = 0;
+    int Lp = 0;
+    for (int m2 = mm; m2 < M; ++m2) {
+      const int2 q2 = pr[m2][tid];
+      if (((part >> m2) & 1) && q2.x == p.x && q2.y == p.y) {
+        mask |= 1u << m2;
+        Lp = max(Lp, len_s[m2]);
+      }
+    }
+    const int nvalid = min(kTile, Lp - kb);   // >= 1: every member here has L > kb
+    st16(out, u32x4{(uint32_t)(kb | (nvalid - 1)), (uint32_t)p.x, (uint32_t)p.y, mask});
+    out += 4;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// 2. Units: region r (group r / n_chunks) holds n_passes[r] passes; it is cut into
+// ceil(n / kUnitPasses) units, numbered in region order.  One workgroup.
+__global__ __launch_bounds__(1024) void decode_units_kernel(GqaDecodeArgs a) {
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = a.dims.n_groups * a.dims.n_chunks;
+  int running = 0;
+  for (int base = 0; base < n; base += 1024) {
+    const int r = base + tid;
+    const int np = r < n ? a.n_passes[r] : 0;
+    const int nu = (np + kUnitPasses - 1) / kUnitPasses;
+    int x = nu;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int off = x - nu, total = 0;
+    for (int w = 0; w < 16; ++w) {
+      off += w < wave ? wsum[w] : 0;
+      total += wsum[w];
+    }
+    __syncthreads();
+    if (r < n) {
+      const int u0 = running + off;
+      a.unit_start[r] = u0;
+      const uint32_t g = (uint32_t)(r / a.dims.n_chunks);
+      const uint32_t p0 = (uint32_t)((size_t)r * a.dims.region_cap);
+      for (int k = 0; k < nu; ++k)
+        st16(a.units + (size_t)(u0 + k) * 4,
+             u32x4{g, p0 + (uint32_t)(k * kUnitPasses), p0 + (uint32_t)min((k + 1) * kUnitPasses, np), 0u});
+    }
+    running += total;
+  }
+  if (tid == 0) {
+    a.unit_start[n] = running;
+    a.queue[0] = 0;
+    a.queue[1] = running * a.num_kv_heads;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// 3. Attention over the passes of one unit and KV head per workgroup iteration.
 template <int D>
 struct DecodeSmem {
   static constexpr int kVStride = D + 16;   // bf16 per V row: 32-byte pad, conflict-free tr reads
   static constexpr int kQStride = D + 8;    // bf16 per Q row: 16-byte pad
   uint16_t v[kWaves][kTile * kVStride];
   uint16_t q[32 * kQStride];
-  int32_t bt[32][kDecodeSplitGqa / 16 + 1];  // the group's block ids for this split (-1: none)
+  u32x4 desc[kUnitPasses];
 };
 
-__device__ __forceinline__ int members_per_group(int R) { return R >= 32 ? 1 : 32 / R; }
-
-// One distinct (block pair) pass of a tile.
 struct Pass {
-  int kb, bA, bB, Lp;
+  int kb, nv, bA, bB;
   bool in;
 };
 
@@ -68,289 +215,281 @@ __global__ __launch_bounds__(256, 2) void gqa_decode_kernel(GqaDecodeArgs a) {
   using Sm = DecodeSmem<D>;
   __shared__ __attribute__((aligned(16))) Sm sm;
   __shared__ float mrg_ml[2][2][32];
+  __shared__ int item_s;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c32 = lane & 31, h32 = lane >> 5;
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
   const int G = Hq / Hkv, T = a.q_per_seq, R = T * G;
-  const int M = members_per_group(R);
-  const int n_groups = (a.num_seqs + M - 1) / M;
-  const int units = n_groups * Hkv;
-  const int split = blockIdx.x / units;
-  const int grp = (blockIdx.x % units) / Hkv;
-  const int g = blockIdx.x % Hkv;
-  const int s0 = grp * M;
-
-  // ---- this lane's query row: member m, token t, head hh
+  const int M = a.dims.members;
   const int m = c32 / R, rr = c32 % R;
-  const int s = s0 + m;
-  const bool row_ok = (m < M) && (s < a.num_seqs);
-  const int L = row_ok ? min(a.context_len[s], a.max_context_len) : 0;
   const int t = rr / G, hh = rr % G;
-  const int pos = L - T + t;                      // keys <= pos are visible
-  int Lg = L;                                     // group-wide longest context
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) Lg = max(Lg, __shfl_xor(Lg, o));
-  const int k_begin = split * kDecodeSplitGqa;
-  if (k_begin >= Lg) return;                      // uniform for the whole workgroup
-  const int k_end = min(Lg, k_begin + kDecodeSplitGqa);
+  const int n_items = a.queue[1];
   const size_t head_stride = (size_t)16 * D;
-
-  // ---- the group's block-table slice for this split -> LDS (validated ids, -1 = none),
-  // so the pass loop never waits on a global load before issuing its K/V loads
-  const int lb_base = k_begin >> 4;
-  const int n_lb = ((k_end + 15) >> 4) - lb_base;
-  for (int c = tid; c < M * n_lb; c += 256) {
-    const int mm = c / n_lb, j = c % n_lb, sm_ = s0 + mm;
-    int b = -1;
-    if (sm_ < a.num_seqs) {
-      const int Lm = min(a.context_len[sm_], a.max_context_len);
-      b = phys_block(a.bt + (size_t)sm_ * a.bt_stride, lb_base + j, (Lm + 15) >> 4, a.num_blocks);
-    }
-    sm.bt[mm][j] = b;
-  }
-  // ---- Q of the group's 32 rows -> LDS once per workgroup (B operand of S^T = K Q^T)
-  for (int c = tid; c < 32 * DC; c += 256) {
-    const int r = c / DC, dc = c % DC;
-    const int mr = r / R, rr2 = r % R, sr = s0 + mr;
-    u32x4 v = {0, 0, 0, 0};
-    if (mr < M && sr < a.num_seqs)
-      v = ld16(a.q + ((size_t)(sr * T + rr2 / G) * Hq + g * G + rr2 % G) * D + 8 * dc);
-    st16(sm.q + r * Sm::kQStride + 8 * dc, v);
-  }
-  __syncthreads();
-
-  f32x16 acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
   uint16_t* vs = sm.v[wave];
 
-  // rows of the group that reach past a tile need no zeroing of that tile's V rows
-  int Lmin = row_ok ? L : 0x7fffffff;
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) Lmin = min(Lmin, __shfl_xor(Lmin, o));
+  for (;;) {
+    if (tid == 0) item_s = atomicAdd(&a.queue[0], 1);
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(item_s);
+    if (item >= n_items) break;                     // uniform for the whole workgroup
+    const int g = item % Hkv, unit = item / Hkv;
+    const u32x4 ud = ld16(a.units + (size_t)unit * 4);
+    const int grp = (int)__builtin_amdgcn_readfirstlane(ud.x);
+    const int p_begin = (int)__builtin_amdgcn_readfirstlane(ud.y);
+    const int np = (int)__builtin_amdgcn_readfirstlane(ud.z) - p_begin;
+    const int s0 = grp * M;
 
-  // ---- pass iterator over this wave's tiles (kb = k_begin + 32 w, + 128, ...)
-  int it_kb = k_begin + wave * kTile - kWaves * kTile;
-  uint64_t it_todo = 0;
-  int it_p0 = -1, it_p1 = -1;
-  auto next_pass = [&](Pass& P) -> bool {
-    while (it_todo == 0) {
-      it_kb += kWaves * kTile;
-      if (it_kb >= k_end) return false;
-      const int j0 = (it_kb >> 4) - lb_base;
-      it_p0 = row_ok ? sm.bt[m][j0] : -1;
-      it_p1 = (row_ok && j0 + 1 < n_lb) ? sm.bt[m][j0 + 1] : -1;
-      it_todo = __ballot((it_p0 >= 0 || it_p1 >= 0) && h32 == 0);
+    // ---- this lane's query row: member m, token t, head hh
+    const int s = s0 + m;
+    const bool row_ok = (m < M) && (s < a.num_seqs);
+    const int L = row_ok ? min(max(a.context_len[s], 0), a.max_context_len) : 0;
+    const int pos = L - T + t;                      // keys <= pos are visible
+
+    // ---- the unit's pass descriptors and the group's 32 query rows -> LDS
+    if (tid < np) sm.desc[tid] = ld16(a.passes + ((size_t)p_begin + tid) * 4);
+    for (int c = tid; c < 32 * DC; c += 256) {
+      const int r = c / DC, dc = c % DC;
+      const int mr = r / R, rr2 = r % R, sr = s0 + mr;
+      u32x4 v = {0, 0, 0, 0};
+      if (mr < M && sr < a.num_seqs)
+        v = ld16(a.q + ((size_t)(sr * T + rr2 / G) * Hq + g * G + rr2 % G) * D + 8 * dc);
+      st16(sm.q + r * Sm::kQStride + 8 * dc, v);
     }
-    const int lead = __builtin_ctzll(it_todo);
-    P.kb = it_kb;
-    P.bA = __builtin_amdgcn_readlane(it_p0, lead);
-    P.bB = __builtin_amdgcn_readlane(it_p1, lead);
-    P.in = (it_p0 == P.bA) && (it_p1 == P.bB);
-    it_todo &= ~__ballot(P.in && h32 == 0);
-    if (it_kb + kTile <= Lmin) {
-      P.Lp = 0x7fffffff;                          // interior tile: every key is valid data
-    } else {                                      // longest context among the pass's rows
-      int lp = P.in ? L : 0;
+    __syncthreads();
+
+    f32x16 acc[MT];
 #pragma unroll
-      for (int o = 16; o > 0; o >>= 1) lp = max(lp, __shfl_xor(lp, o));
-      P.Lp = lp;
-    }
-    return true;
-  };
-  // K rows straight into the A operand (lane: key c32 of the pass); V as 4 keys x 8 dims.
-  // Interior passes (both blocks present, no tail) take an unconditional path.
-  auto issue = [&](const Pass& P, u32x4 (&kf)[KS], u32x4 (&vr)[VG][4]) {
-    if (P.bA >= 0 && P.bB >= 0 && P.Lp == 0x7fffffff) {
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // ---- this wave's passes: wave, wave + 4, ... of the unit
+    int it = wave;
+    auto next_pass = [&](Pass& P) -> bool {
+      if (it >= np) return false;
+      const u32x4 d = sm.desc[it];
+      it += kWaves;
+      const uint32_t d0 = __builtin_amdgcn_readfirstlane(d.x);
+      P.kb = (int)(d0 & ~31u);
+      P.nv = (int)(d0 & 31u) + 1;
+      P.bA = (int)__builtin_amdgcn_readfirstlane(d.y);
+      P.bB = (int)__builtin_amdgcn_readfirstlane(d.z);
+      const uint32_t mask = __builtin_amdgcn_readfirstlane(d.w);
+      P.in = row_ok && ((mask >> m) & 1u);
+      return true;
+    };
+    // K rows straight into the A operand (lane: key c32 of the pass); V as 4 keys x 8 dims.
+    // Interior passes (both blocks present, all 32 keys hold data) take an unconditional path.
+    auto issue = [&](const Pass& P, u32x4 (&kf)[KS], u32x4 (&vr)[VG][4]) {
+      if (P.bA >= 0 && P.bB >= 0 && P.nv == kTile) {
+        const int blk = c32 < 16 ? P.bA : P.bB;
+        const uint16_t* kp = a.k + ((size_t)blk * Hkv + g) * head_stride + (size_t)(c32 & 15) * D + 8 * h32;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[ks] = ld16(kp + 16 * ks);
+#pragma unroll
+        for (int j = 0; j < VG; ++j) {
+          const int gi = lane + 64 * j, dc = gi % DC, kg = gi / DC;
+          const int vb = kg < 4 ? P.bA : P.bB;
+          const uint16_t* vp = a.v + ((size_t)vb * Hkv + g) * head_stride + (size_t)(4 * (kg & 3)) * D + 8 * dc;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vr[j][e] = ld16(vp + (size_t)e * D);
+        }
+        return;
+      }
       const int blk = c32 < 16 ? P.bA : P.bB;
-      const uint16_t* kp = a.k + ((size_t)blk * Hkv + g) * head_stride + (size_t)(c32 & 15) * D + 8 * h32;
+      if (blk >= 0) {
+        const uint16_t* kp = a.k + ((size_t)blk * Hkv + g) * head_stride + (size_t)(c32 & 15) * D + 8 * h32;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[ks] = ld16(kp + 16 * ks);
+        for (int ks = 0; ks < KS; ++ks) kf[ks] = ld16(kp + 16 * ks);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[ks] = u32x4{0, 0, 0, 0};
+      }
 #pragma unroll
       for (int j = 0; j < VG; ++j) {
         const int gi = lane + 64 * j, dc = gi % DC, kg = gi / DC;
         const int vb = kg < 4 ? P.bA : P.bB;
-        const uint16_t* vp = a.v + ((size_t)vb * Hkv + g) * head_stride + (size_t)(4 * (kg & 3)) * D + 8 * dc;
+        if (vb >= 0) {
+          const uint16_t* vp = a.v + ((size_t)vb * Hkv + g) * head_stride + (size_t)(4 * (kg & 3)) * D + 8 * dc;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vr[j][e] = ld16(vp + (size_t)e * D);
+          for (int e = 0; e < 4; ++e)
+            vr[j][e] = (4 * kg + e < P.nv) ? ld16(vp + (size_t)e * D) : u32x4{0, 0, 0, 0};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vr[j][e] = u32x4{0, 0, 0, 0};
+        }
       }
-      return;
-    }
-    const int blk = c32 < 16 ? P.bA : P.bB;
-    if (blk >= 0) {
-      const uint16_t* kp = a.k + ((size_t)blk * Hkv + g) * head_stride + (size_t)(c32 & 15) * D + 8 * h32;
+    };
+    const int m16 = lane & 15, gq = (lane >> 4) & 1;
+    Pass nxt;
+    u32x4 kfA[KS], kfB[KS], vr_n[VG][4];
+    // One pass with its K in kf; the next pass is issued into kf_o (ping-pong) and vr_n.
+    auto process = [&](u32x4 (&kf)[KS], u32x4 (&kf_o)[KS]) -> bool {
+      const Pass cur = nxt;
+      // ---- V (bf16) -> LDS row-major; frees the V registers for the next pass
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[ks] = ld16(kp + 16 * ks);
-    } else {
+      for (int j = 0; j < VG; ++j) {
+        const int gi = lane + 64 * j, dc = gi % DC, kg = gi / DC;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[ks] = u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int j = 0; j < VG; ++j) {
-      const int gi = lane + 64 * j, dc = gi % DC, kg = gi / DC;
-      const int vb = kg < 4 ? P.bA : P.bB;
-      if (vb >= 0) {
-        const uint16_t* vp = a.v + ((size_t)vb * Hkv + g) * head_stride + (size_t)(4 * (kg & 3)) * D + 8 * dc;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          vr[j][e] = (P.kb + 4 * kg + e < P.Lp) ? ld16(vp + (size_t)e * D) : u32x4{0, 0, 0, 0};
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vr[j][e] = u32x4{0, 0, 0, 0};
+        for (int e = 0; e < 4; ++e) st16(vs + (4 * kg + e) * Sm::kVStride + 8 * dc, vr_n[j][e]);
       }
-    }
-  };
-  const int m16 = lane & 15, gq = (lane >> 4) & 1;
-  Pass nxt;
-  u32x4 kfA[KS], kfB[KS], vr_n[VG][4];
-  // One pass with its K in kf; the next pass is issued into kf_o (ping-pong) and vr_n.
-  auto process = [&](u32x4 (&kf)[KS], u32x4 (&kf_o)[KS]) -> bool {
-    const Pass cur = nxt;
-    // ---- V (bf16) -> LDS row-major; frees the V registers for the next pass
+      // the next pass's loads are in flight while this one is computed
+      const bool more = next_pass(nxt);
+      if (more) issue(nxt, kf_o, vr_n);
+      // ---- S^T = K Q^T (Q^T fragments from LDS)
+      const uint16_t* qp = sm.q + c32 * Sm::kQStride + 8 * h32;
+      f32x16 sacc = mfma32x32x16(kf[0], *reinterpret_cast<const u32x4*>(qp), f32x16{});
 #pragma unroll
-    for (int j = 0; j < VG; ++j) {
-      const int gi = lane + 64 * j, dc = gi % DC, kg = gi / DC;
+      for (int ks = 1; ks < KS; ++ks)
+        sacc = mfma32x32x16(kf[ks], *reinterpret_cast<const u32x4*>(qp + 16 * ks), sacc);
+      // ---- mask + online softmax (log2 domain); lane = one row, 16 keys
+      float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) st16(vs + (4 * kg + e) * Sm::kVStride + 8 * dc, vr_n[j][e]);
-    }
-    // the next pass's loads are in flight while this one is computed
-    const bool more = next_pass(nxt);
-    if (more) issue(nxt, kf_o, vr_n);
-    // ---- S^T = K Q^T (Q^T fragments from LDS)
-    const uint16_t* qp = sm.q + c32 * Sm::kQStride + 8 * h32;
-    f32x16 sacc = mfma32x32x16(kf[0], *reinterpret_cast<const u32x4*>(qp), f32x16{});
-#pragma unroll
-    for (int ks = 1; ks < KS; ++ks)
-      sacc = mfma32x32x16(kf[ks], *reinterpret_cast<const u32x4*>(qp + 16 * ks), sacc);
-    // ---- mask + online softmax (log2 domain); lane = one row, 16 keys
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = cur.kb + 8 * (i >> 2) + 4 * h32 + (i & 3);
-      const float v = (cur.in && key <= pos) ? sacc[i] * a.scale_log2 : -INFINITY;
-      sacc[i] = v;
-      mx = fmaxf(mx, v);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    // rescale only when some row's running max moved (exact: alpha = 1 otherwise)
-    if (__ballot(m_new > m_run) != 0) {
-      const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
-      m_run = m_new;
-    }
-    float rs = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = m_run == -INFINITY ? 0.f : fast_exp2(sacc[i] - m_run);
-      sacc[i] = p;
-      rs += p;
-    }
-    l_run += rs;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      // P = P_hi + P_lo, both bf16: the pair carries ~16 significant bits of P
-      u32x4 ph, pl;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float a0 = sacc[8 * ks + 2 * w], a1 = sacc[8 * ks + 2 * w + 1];
-        const uint32_t hv = pack_bf16x2(a0, a1);
-        ph[w] = hv;
-        pl[w] = pack_bf16x2(a0 - __uint_as_float(hv << 16), a1 - __uint_as_float(hv & 0xffff0000u));
+      for (int i = 0; i < 16; ++i) {
+        const int key = cur.kb + 8 * (i >> 2) + 4 * h32 + (i & 3);
+        const float v = (cur.in && key <= pos) ? sacc[i] * a.scale_log2 : -INFINITY;
+        sacc[i] = v;
+        mx = fmaxf(mx, v);
       }
-      // this lane's keys: kbase + 0..3 and kbase + 8..11 (the P^T register order)
-      const int kbase = 16 * ks + 4 * h32;
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      // rescale only when some row's running max moved (exact: alpha = 1 otherwise)
+      if (__ballot(m_new > m_run) != 0) {
+        const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint16_t* vp = vs + (kbase + (m16 >> 2)) * Sm::kVStride + 32 * mt + 16 * gq + 4 * (m16 & 3);
-        const u32x2 lo = lds_read_tr16(vp);
-        const u32x2 hi = lds_read_tr16(vp + 8 * Sm::kVStride);
-        const u32x4 va = u32x4{lo.x, lo.y, hi.x, hi.y};
-        acc[mt] = mfma32x32x16(va, ph, acc[mt]);
-        acc[mt] = mfma32x32x16(va, pl, acc[mt]);
+        for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+        m_run = m_new;
       }
+      float rs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = m_run == -INFINITY ? 0.f : fast_exp2(sacc[i] - m_run);
+        sacc[i] = p;
+        rs += p;
+      }
+      l_run += rs;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        // P = P_hi + P_lo, both bf16: the pair carries ~16 significant bits of P
+        u32x4 ph, pl;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float a0 = sacc[8 * ks + 2 * w], a1 = sacc[8 * ks + 2 * w + 1];
+          const uint32_t hv = pack_bf16x2(a0, a1);
+          ph[w] = hv;
+          pl[w] = pack_bf16x2(a0 - __uint_as_float(hv << 16), a1 - __uint_as_float(hv & 0xffff0000u));
+        }
+        // this lane's keys: kbase + 0..3 and kbase + 8..11 (the P^T register order)
+        const int kbase = 16 * ks + 4 * h32;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const uint16_t* vp = vs + (kbase + (m16 >> 2)) * Sm::kVStride + 32 * mt + 16 * gq + 4 * (m16 & 3);
+          const u32x2 lo = lds_read_tr16(vp);
+          const u32x2 hi = lds_read_tr16(vp + 8 * Sm::kVStride);
+          const u32x4 va = u32x4{lo.x, lo.y, hi.x, hi.y};
+          acc[mt] = mfma32x32x16(va, ph, acc[mt]);
+          acc[mt] = mfma32x32x16(va, pl, acc[mt]);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      return more;
+    };
+    bool have = next_pass(nxt);
+    if (have) issue(nxt, kfA, vr_n);
+    while (have) {
+      have = process(kfA, kfB);
+      if (!have) break;
+      have = process(kfB, kfA);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    return more;
-  };
-  bool have = next_pass(nxt);
-  if (have) issue(nxt, kfA, vr_n);
-  while (have) {
-    have = process(kfA, kfB);
-    if (!have) break;
-    have = process(kfB, kfA);
-  }
 
-  // ---- merge the 4 wave states pairwise in a fixed order: (w0+w2) + (w1+w3)
-  l_run += __shfl_xor(l_run, 32);
-  float* buf = reinterpret_cast<float*>(&sm.v[0][0]);   // [2][32 rows][D] floats
-  auto put = [&](int slot) {
+    // ---- merge the 4 wave states pairwise in a fixed order: (w0+w2) + (w1+w3)
+    l_run += __shfl_xor(l_run, 32);
+    float* buf = reinterpret_cast<float*>(&sm.v[0][0]);   // [2][32 rows][D] floats
+    auto put = [&](int slot) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<f32x4*>(buf + ((size_t)slot * 32 + c32) * D + 32 * mt + 8 * q4 + 4 * h32) =
-            f32x4{acc[mt][4 * q4], acc[mt][4 * q4 + 1], acc[mt][4 * q4 + 2], acc[mt][4 * q4 + 3]};
-    if (h32 == 0) { mrg_ml[slot][0][c32] = m_run; mrg_ml[slot][1][c32] = l_run; }
-  };
-  auto take = [&](int slot) {
-    const float mo = mrg_ml[slot][0][c32], lo = mrg_ml[slot][1][c32];
-    const float Mx = fmaxf(m_run, mo);
-    const float sa = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - Mx);
-    const float sb = (mo == -INFINITY) ? 0.f : fast_exp2(mo - Mx);
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(buf + ((size_t)slot * 32 + c32) * D + 32 * mt + 8 * q4 + 4 * h32) =
+              f32x4{acc[mt][4 * q4], acc[mt][4 * q4 + 1], acc[mt][4 * q4 + 2], acc[mt][4 * q4 + 3]};
+      if (h32 == 0) { mrg_ml[slot][0][c32] = m_run; mrg_ml[slot][1][c32] = l_run; }
+    };
+    auto take = [&](int slot) {
+      const float mo = mrg_ml[slot][0][c32], lo = mrg_ml[slot][1][c32];
+      const float Mx = fmaxf(m_run, mo);
+      const float sa = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - Mx);
+      const float sb = (mo == -INFINITY) ? 0.f : fast_exp2(mo - Mx);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 o = *reinterpret_cast<const f32x4*>(buf + ((size_t)slot * 32 + c32) * D + 32 * mt + 8 * q4 + 4 * h32);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 o = *reinterpret_cast<const f32x4*>(buf + ((size_t)slot * 32 + c32) * D + 32 * mt + 8 * q4 + 4 * h32);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][4 * q4 + i] = acc[mt][4 * q4 + i] * sa + o[i] * sb;
-      }
-    l_run = l_run * sa + lo * sb;
-    m_run = Mx;
-  };
-  __syncthreads();
-  if (wave >= 2) put(wave - 2);
-  __syncthreads();
-  if (wave < 2) take(wave);
-  __syncthreads();
-  if (wave == 1) put(0);
-  __syncthreads();
-  if (wave != 0) return;
-  take(0);
-  if (!row_ok) return;
-  const int TR = T * Hq;
-  const size_t pidx = ((size_t)s * a.max_splits + split) * TR + (size_t)t * Hq + g * G + hh;
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  float* op = a.part_o + pidx * D;
+          for (int i = 0; i < 4; ++i) acc[mt][4 * q4 + i] = acc[mt][4 * q4 + i] * sa + o[i] * sb;
+        }
+      l_run = l_run * sa + lo * sb;
+      m_run = Mx;
+    };
+    __syncthreads();
+    if (wave >= 2) put(wave - 2);
+    __syncthreads();
+    if (wave < 2) take(wave);
+    __syncthreads();
+    if (wave == 1) put(0);
+    __syncthreads();
+    if (wave == 0) {
+      take(0);
+      // every row is written (rows of members outside the unit get lse = -inf); the
+      // combine reads only the rows of real sequences
+      const size_t pidx = (size_t)item * 32 + c32;
+      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+      float* op = a.part_o + pidx * D;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      *reinterpret_cast<f32x4*>(op + 32 * mt + 8 * q4 + 4 * h32) =
-          f32x4{acc[mt][4 * q4] * inv, acc[mt][4 * q4 + 1] * inv, acc[mt][4 * q4 + 2] * inv, acc[mt][4 * q4 + 3] * inv};
-  if (h32 == 0) a.part_lse[pidx] = l_run > 0.f ? m_run + __log2f(l_run) : -INFINITY;
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(op + 32 * mt + 8 * q4 + 4 * h32) =
+              f32x4{acc[mt][4 * q4] * inv, acc[mt][4 * q4 + 1] * inv, acc[mt][4 * q4 + 2] * inv, acc[mt][4 * q4 + 3] * inv};
+      if (h32 == 0) a.part_lse[pidx] = l_run > 0.f ? m_run + __log2f(l_run) : -INFINITY;
+    }
+  }  // work items
+}
+
+// Resident workgroups of the persistent decode grid: two per compute unit.
+int decode_grid(int units_cap, int num_kv_heads) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  const long items = (long)units_cap * num_kv_heads;
+  return (int)std::min<long>(items, 2L * cus[dev]);
 }
 
 }  // namespace
 
+hipError_t launch_gqa_decode_plan(const GqaDecodeArgs& a, hipStream_t stream) {
+  const unsigned regions = (unsigned)a.dims.n_groups * a.dims.n_chunks;
+  if (regions == 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(regions), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(decode_units_kernel, dim3(1), dim3(1024), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gqa_decode(const GqaDecodeArgs& a, hipStream_t stream) {
-  const int R = a.q_per_seq * (a.num_q_heads / a.num_kv_heads);
-  const int M = R >= 32 ? 1 : 32 / R;
-  const unsigned n_groups = (unsigned)((a.num_seqs + M - 1) / M);
-  const unsigned grid = (unsigned)a.max_splits * n_groups * a.num_kv_heads;
-  if (grid == 0) return hipSuccess;
+  if (a.dims.n_groups == 0 || a.dims.n_chunks == 0) return hipSuccess;
+  const int grid = decode_grid(a.dims.units_cap, a.num_kv_heads);
   if (a.head_dim == 128)
     hipLaunchKernelGGL((gqa_decode_kernel<128>), dim3(grid), dim3(256), 0, stream, a);
   else
@@ -359,45 +498,96 @@ hipError_t launch_gqa_decode(const GqaDecodeArgs& a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------------
-// Fixed-order combine of split partials: for each (sequence, row) with n splits,
-//   M = max_j lse_j,  o = sum_j 2^(lse_j - M) o_j / sum_j 2^(lse_j - M),
-// summed for j = 0 .. n-1 in order, so results are identical run to run.
+// 4. Fixed-order combine of partials: for each (sequence, row) with n partials,
+//   o = sum_j 2^(lse_j - M) o_j / sum_j 2^(lse_j - M),  M = max_j lse_j.
+// A workgroup takes one (sequence, row): its threads form JL lanes over the partials
+// (lane jl takes j = jl, jl + JL, ...) times D/4 lanes over the dimensions; each lane
+// keeps an online (max, sum, weighted sum) and the JL lane states are merged in lane
+// order, so the result is identical run to run.
 namespace {
+constexpr int kCombineBatch = 8;   // partials loaded per lane before they are used
+
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  __shared__ f32x4 num_s[256];
+  __shared__ float m_s[256], den_s[256];
   const int row = blockIdx.x % a.rows, s = blockIdx.x / a.rows;
-  const int L = min(a.context_len[s], a.max_context_len);
-  const int n = L > 0 ? (L + a.split - 1) / a.split : 0;
-  const size_t stride = (size_t)a.rows;
-  const float* lse_p = a.part_lse + (size_t)s * a.max_splits * stride + row;
-  float M = -INFINITY;
-  for (int j = 0; j < n; ++j) M = fmaxf(M, lse_p[j * stride]);
-  float den = 0.f;
-  for (int j = 0; j < n; ++j) {
-    const float lj = lse_p[j * stride];
-    den += (M == -INFINITY || lj == -INFINITY) ? 0.f : fast_exp2(lj - M);
+  const int D = a.head_dim, DV4 = D / 4, JL = 256 / DV4;
+  const int tid = threadIdx.x, jl = tid / DV4, d4 = tid % DV4;
+  size_t base;
+  long stride;
+  int n;
+  if (a.unit_start != nullptr) {
+    const int Hq = a.rows / a.q_per_seq, G = Hq / a.num_kv_heads, R = a.q_per_seq * G;
+    const int t = row / Hq, hq = row % Hq, head = hq / G;
+    const int g = s / a.members, m = s % a.members;
+    const int u0 = a.unit_start[g * a.n_chunks], u1 = a.unit_start[(g + 1) * a.n_chunks];
+    n = u1 - u0;
+    base = ((size_t)u0 * a.num_kv_heads + head) * 32 + m * R + t * G + hq % G;
+    stride = (long)a.num_kv_heads * 32;
+  } else {
+    const int L = min(max(a.context_len[s], 0), a.max_context_len);
+    n = L > 0 ? (L + a.split - 1) / a.split : 0;
+    base = (size_t)s * a.max_splits * a.rows + row;
+    stride = a.rows;
   }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  const float* o_p = a.part_o + ((size_t)s * a.max_splits * stride + row) * a.head_dim;
-  uint16_t* out = a.out + ((size_t)s * a.rows + row) * a.head_dim;
-  for (int d = threadIdx.x; d < a.head_dim; d += blockDim.x) {
-    float num = 0.f;
-    for (int j = 0; j < n; ++j) {
-      const float lj = lse_p[j * stride];
-      const float w = (M == -INFINITY || lj == -INFINITY) ? 0.f : fast_exp2(lj - M);
-      num += w * o_p[(size_t)j * stride * a.head_dim + d];
+  float mx = -INFINITY, den = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = jl; j0 < n; j0 += JL * kCombineBatch) {
+    float lj[kCombineBatch];
+    f32x4 oj[kCombineBatch];
+#pragma unroll
+    for (int b = 0; b < kCombineBatch; ++b) {
+      const int j = j0 + b * JL;
+      const size_t slot = base + (size_t)j * stride;
+      lj[b] = j < n ? a.part_lse[slot] : -INFINITY;
+      oj[b] = j < n ? *reinterpret_cast<const f32x4*>(a.part_o + slot * D + 4 * d4) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    out[d] = __builtin_bit_cast(uint16_t, (__bf16)(num * inv));
+#pragma unroll
+    for (int b = 0; b < kCombineBatch; ++b) {
+      if (lj[b] == -INFINITY) continue;
+      if (lj[b] > mx) {
+        const float sc = mx == -INFINITY ? 0.f : fast_exp2(mx - lj[b]);
+        den *= sc;
+        num *= sc;
+        mx = lj[b];
+      }
+      const float w = fast_exp2(lj[b] - mx);
+      den += w;
+      num += w * oj[b];
+    }
   }
-  if (a.lse != nullptr && threadIdx.x == 0)
-    a.lse[(size_t)s * a.rows + row] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
+  num_s[tid] = num;
+  m_s[tid] = mx;
+  den_s[tid] = den;
+  __syncthreads();
+  if (jl != 0) return;
+  float M = -INFINITY;
+  for (int k = 0; k < JL; ++k) M = fmaxf(M, m_s[k * DV4 + d4]);
+  float tden = 0.f;
+  f32x4 tnum = {0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
+    for (int k = 0; k < JL; ++k) {
+      const float mk = m_s[k * DV4 + d4];
+      if (mk == -INFINITY) continue;
+      const float w = fast_exp2(mk - M);
+      tden += w * den_s[k * DV4 + d4];
+      tnum += w * num_s[k * DV4 + d4];
+    }
+  }
+  const float inv = tden > 0.f ? 1.f / tden : 0.f;
+  uint16_t* out = a.out + ((size_t)s * a.rows + row) * D + 4 * d4;
+  const f32x2 lo = {tnum[0] * inv, tnum[1] * inv}, hi = {tnum[2] * inv, tnum[3] * inv};
+  *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf16x2(lo.x, lo.y), pack_bf16x2(hi.x, hi.y)};
+  if (a.lse != nullptr && d4 == 0)
+    a.lse[(size_t)s * a.rows + row] = tden > 0.f ? (M + __log2f(tden)) * kLn2 : -INFINITY;
 }
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)a.num_seqs * a.rows;
   if (grid == 0) return hipSuccess;
-  const int threads = a.head_dim >= 256 ? 256 : a.head_dim;
-  hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(threads), 0, stream, a);
+  if (a.head_dim % 4 != 0 || a.head_dim / 4 > 256 || 256 % (a.head_dim / 4) != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -94,28 +94,43 @@ hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
     if (st_ != PA_OK) return st_;       \
   } while (0)
 
-// ---- decode workspace layout: partial outputs then partial log2-sum-exp
+// ---- decode workspace layouts
+// MLA: partial outputs [S][max_splits][rows][512] then partial log2-sum-exp.
+// GQA: unit partials, partial log2-sum-exp, the pass lists, pass counts, unit starts,
+// the unit table and the work queue (each part 256-byte aligned).
 struct DecodeLayout {
   int max_splits, rows, d_v, split;
-  size_t o_bytes, lse_bytes;
-  size_t total() const { return o_bytes + lse_bytes; }
+  pa::GqaDecodeDims dims;
+  size_t o_bytes, lse_bytes, pass_bytes, npass_bytes, ustart_bytes, unit_bytes, queue_bytes;
+  size_t total() const {
+    return o_bytes + lse_bytes + pass_bytes + npass_bytes + ustart_bytes + unit_bytes + queue_bytes;
+  }
 };
 
-DecodeLayout decode_layout(int num_seqs, int q_per_seq, int num_q_heads, int max_context_len, bool mla) {
-  DecodeLayout l;
-  l.split = mla ? pa::kDecodeSplitMla : pa::kDecodeSplitGqa;
-  l.max_splits = max_context_len > 0 ? ceil_div(max_context_len, l.split) : 0;
+DecodeLayout decode_layout(int num_seqs, int q_per_seq, int num_q_heads, int max_context_len,
+                           const pa_kv_pool* pool) {
+  DecodeLayout l{};
   l.rows = q_per_seq * num_q_heads;
-  l.d_v = 0;
-  l.o_bytes = 0;
-  l.lse_bytes = 0;
+  l.d_v = pool->head_dim_v;
+  if (!is_gqa_pool(pool)) {
+    l.split = pa::kDecodeSplitMla;
+    l.max_splits = max_context_len > 0 ? ceil_div(max_context_len, l.split) : 0;
+    l.o_bytes = round_up((size_t)num_seqs * l.max_splits * l.rows * l.d_v * sizeof(float), 256);
+    l.lse_bytes = round_up((size_t)num_seqs * l.max_splits * l.rows * sizeof(float), 256);
+    return l;
+  }
+  const int hkv = pool->num_kv_heads;
+  l.dims = pa::gqa_decode_dims(num_seqs, q_per_seq, num_q_heads, hkv, max_context_len);
+  const size_t regions = (size_t)l.dims.n_groups * l.dims.n_chunks;
+  const size_t slots = (size_t)l.dims.units_cap * hkv * 32;
+  l.o_bytes = round_up(slots * l.d_v * sizeof(float), 256);
+  l.lse_bytes = round_up(slots * sizeof(float), 256);
+  l.pass_bytes = round_up(regions * l.dims.region_cap * 16, 256);
+  l.npass_bytes = round_up(regions * sizeof(int32_t), 256);
+  l.ustart_bytes = round_up((regions + 1) * sizeof(int32_t), 256);
+  l.unit_bytes = round_up((size_t)l.dims.units_cap * 16, 256);
+  l.queue_bytes = 256;
   return l;
-}
-
-void finish_layout(DecodeLayout& l, int num_seqs, int d_v) {
-  l.d_v = d_v;
-  l.o_bytes = round_up((size_t)num_seqs * l.max_splits * l.rows * d_v * sizeof(float), 256);
-  l.lse_bytes = round_up((size_t)num_seqs * l.max_splits * l.rows * sizeof(float), 256);
 }
 
 }  // namespace
@@ -217,10 +232,8 @@ static pa_status check_decode(const pa_kv_pool* pool, int32_t num_seqs, int32_t 
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t q_per_seq, int32_t num_q_heads,
                                         int32_t max_context_len, const pa_kv_pool* pool) {
   if (pool == nullptr || num_seqs < 0 || q_per_seq < 1 || num_q_heads < 1 || max_context_len < 0) return 0;
-  const bool mla = !is_gqa_pool(pool);
-  DecodeLayout l = decode_layout(num_seqs, q_per_seq, num_q_heads, max_context_len, mla);
-  finish_layout(l, num_seqs, pool->head_dim_v);
-  return l.total();
+  if (is_gqa_pool(pool) && (pool->num_kv_heads < 1 || num_q_heads % pool->num_kv_heads != 0)) return 0;
+  return decode_layout(num_seqs, q_per_seq, num_q_heads, max_context_len, pool).total();
 }
 
 pa_status paged_attn_decode(const void* q, const pa_kv_pool* pool, const int32_t* block_table,
@@ -235,17 +248,28 @@ pa_status paged_attn_decode(const void* q, const pa_kv_pool* pool, const int32_t
   if (!aligned(q, 16) || !aligned(out, 16)) return fail(PA_ERR_INVALID_ARG, "q/out must be 16-byte aligned");
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite and > 0");
   const bool mla = !is_gqa_pool(pool);
-  DecodeLayout l = decode_layout(num_seqs, q_per_seq, num_q_heads, max_context_len, mla);
-  finish_layout(l, num_seqs, pool->head_dim_v);
+  const DecodeLayout l = decode_layout(num_seqs, q_per_seq, num_q_heads, max_context_len, pool);
   if (num_seqs == 0 || max_context_len == 0) return PA_OK;
   if (workspace == nullptr || workspace_bytes < l.total())
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", l.total(), workspace_bytes);
   if (!aligned(workspace, 16)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  float* part_o = static_cast<float*>(workspace);
-  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + l.o_bytes);
+  char* ws = static_cast<char*>(workspace);
+  float* part_o = reinterpret_cast<float*>(ws);
+  float* part_lse = reinterpret_cast<float*>(ws + l.o_bytes);
+  pa::CombineArgs c{};
   (void)hipGetLastError();
   if (!mla) {
     pa::GqaDecodeArgs a{};
+    size_t off = l.o_bytes + l.lse_bytes;
+    a.passes = reinterpret_cast<uint32_t*>(ws + off);
+    off += l.pass_bytes;
+    a.n_passes = reinterpret_cast<int32_t*>(ws + off);
+    off += l.npass_bytes;
+    a.unit_start = reinterpret_cast<int32_t*>(ws + off);
+    off += l.ustart_bytes;
+    a.units = reinterpret_cast<uint32_t*>(ws + off);
+    off += l.unit_bytes;
+    a.queue = reinterpret_cast<int32_t*>(ws + off);
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(pool->k);
     a.v = static_cast<const uint16_t*>(pool->v);
@@ -261,9 +285,15 @@ pa_status paged_attn_decode(const void* q, const pa_kv_pool* pool, const int32_t
     a.head_dim = pool->head_dim_qk;
     a.num_blocks = pool->num_blocks;
     a.max_context_len = max_context_len;
-    a.max_splits = l.max_splits;
+    a.dims = l.dims;
     a.scale_log2 = scale * 1.4426950408889634f;
+    PA_TRY(launched(timed("decode_plan", stream, [&] { return pa::launch_gqa_decode_plan(a, stream); }), "decode plan launch"));
     PA_TRY(launched(timed("decode_gqa", stream, [&] { return pa::launch_gqa_decode(a, stream); }), "decode launch"));
+    c.unit_start = a.unit_start;
+    c.members = l.dims.members;
+    c.n_chunks = l.dims.n_chunks;
+    c.num_kv_heads = pool->num_kv_heads;
+    c.q_per_seq = q_per_seq;
   } else {
     pa::MlaDecodeArgs a{};
     a.q = static_cast<const uint16_t*>(q);
@@ -283,7 +313,6 @@ pa_status paged_attn_decode(const void* q, const pa_kv_pool* pool, const int32_t
     a.scale_log2 = scale * 1.4426950408889634f;
     PA_TRY(launched(timed("decode_mla", stream, [&] { return pa::launch_mla_decode(a, stream); }), "MLA decode launch"));
   }
-  pa::CombineArgs c{};
   c.part_o = part_o;
   c.part_lse = part_lse;
   c.context_len = context_len;

@@ -6,16 +6,32 @@
 
 namespace pa {
 
-// Keys per split of the decode key range.  Each split yields a partial (o, lse) pair
+// MLA decode: keys per split of the key range.  Each split yields a partial (o, lse) pair
 // that the combine kernel merges in split order.
-#ifndef PA_DECODE_SPLIT_GQA
-#define PA_DECODE_SPLIT_GQA 1024
-#endif
 #ifndef PA_DECODE_SPLIT_MLA
 #define PA_DECODE_SPLIT_MLA 8192
 #endif
-constexpr int kDecodeSplitGqa = PA_DECODE_SPLIT_GQA;
 constexpr int kDecodeSplitMla = PA_DECODE_SPLIT_MLA;
+
+// GQA decode work units: a group's list of distinct block-pair passes is cut into units
+// of at most kUnitPasses passes (one partial (o, lse) per unit and KV head); the plan
+// covers kPlanTiles 32-key tiles per workgroup.
+#ifndef PA_DECODE_UNIT_PASSES
+#define PA_DECODE_UNIT_PASSES 64
+#endif
+constexpr int kUnitPasses = PA_DECODE_UNIT_PASSES;
+constexpr int kPlanTiles = 256;
+
+// Host-side sizes of the GQA decode workspace (shared by the C ABI and the launcher).
+struct GqaDecodeDims {
+  int32_t members;      // sequences per group: 32 / (q_per_seq * group size), >= 1
+  int32_t n_groups;     // ceil(num_seqs / members)
+  int32_t n_chunks;     // plan chunks per group: ceil(ceil(max_context_len / 32) / kPlanTiles)
+  int32_t region_cap;   // pass capacity of one (group, chunk) region: kPlanTiles * members
+  int32_t units_cap;    // upper bound of units over all groups
+};
+GqaDecodeDims gqa_decode_dims(int num_seqs, int q_per_seq, int num_q_heads, int num_kv_heads,
+                              int max_context_len);
 
 struct GqaPrefillArgs {
   const uint16_t* q;
@@ -38,10 +54,17 @@ struct GqaDecodeArgs {
   const uint16_t* v;
   const int32_t* bt;
   const int32_t* context_len;
-  float* part_o;      // [S][max_splits][T*Hq][D]
-  float* part_lse;    // [S][max_splits][T*Hq], log2 units
+  float* part_o;        // [units_cap * Hkv * 32][D]: unit u, KV head h, tile row r at (u*Hkv+h)*32+r
+  float* part_lse;      // [units_cap * Hkv * 32], log2 units
+  uint32_t* passes;     // [n_groups * n_chunks][region_cap][4]: {key base | (valid keys - 1),
+                        //   block A, block B, member mask}
+  int32_t* n_passes;    // [n_groups * n_chunks]
+  int32_t* unit_start;  // [n_groups * n_chunks + 1]: first unit of each region; total last
+  uint32_t* units;      // [units_cap][4]: {group, first pass, end pass, 0} (pass indices absolute)
+  int32_t* queue;       // [2]: next work item, number of items (units * Hkv)
   int32_t bt_stride, num_seqs, q_per_seq, num_q_heads, num_kv_heads, head_dim, num_blocks;
-  int32_t max_context_len, max_splits;
+  int32_t max_context_len;
+  GqaDecodeDims dims;
   float scale_log2;
 };
 
@@ -52,6 +75,10 @@ struct CombineArgs {
   uint16_t* out;                // [S][rows][D]
   float* lse;                   // [S][rows] or null
   int32_t num_seqs, rows, head_dim, max_splits, split, max_context_len;
+  // GQA unit partials (unit_start != null): row (t, hq) of sequence s reads the units of
+  // its group; otherwise partials are [S][max_splits][rows] with split `split`.
+  const int32_t* unit_start;
+  int32_t members, n_chunks, num_kv_heads, q_per_seq;
 };
 
 struct MlaDecodeArgs {
@@ -114,6 +141,8 @@ struct GatherArgs {
 };
 
 hipError_t launch_gqa_prefill(const GqaPrefillArgs& a, hipStream_t s);
+// GQA decode = plan (pass lists, units, queue reset) then the persistent attention grid.
+hipError_t launch_gqa_decode_plan(const GqaDecodeArgs& a, hipStream_t s);
 hipError_t launch_gqa_decode(const GqaDecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_mla_decode(const MlaDecodeArgs& a, hipStream_t s);
