@@ -86,17 +86,27 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(GqaDecodeArgs a) {
   __syncthreads();
   const int tile = c * kPlanTiles + tid, kb = tile * kTile;
   uint32_t part = 0;                    // members taking part in this tile
-  for (int mm = 0; mm < M; ++mm) {
-    const int L = len_s[mm];
-    int2 p = {-1, -1};
-    if (kb < L) {
-      const int nlb = (L + 15) >> 4;
-      const int32_t* row = a.bt + (size_t)(s0 + mm) * a.bt_stride;
-      p.x = phys_block(row, 2 * tile, nlb, a.num_blocks);
-      p.y = phys_block(row, 2 * tile + 1, nlb, a.num_blocks);
-      part |= 1u << mm;
+  for (int m0 = 0; m0 < M; m0 += 8) {   // 8 members' loads in flight at a time
+    int ra[8], rb[8], nl[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {       // unconditional loads (entry 0 when unused)
+      const int mm = m0 + i;
+      const int L = mm < M ? len_s[mm] : 0;
+      const bool ok = kb < L;
+      nl[i] = ok ? (L + 15) >> 4 : 0;
+      const int32_t* row = a.bt + (ok ? (size_t)(s0 + mm) * a.bt_stride : 0);
+      ra[i] = row[ok ? 2 * tile : 0];
+      rb[i] = row[2 * tile + 1 < nl[i] ? 2 * tile + 1 : 0];
+      if (ok) part |= 1u << mm;
     }
-    pr[mm][tid] = p;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (m0 + i >= M) break;
+      int2 p = {-1, -1};
+      if (2 * tile < nl[i] && ra[i] >= 0 && ra[i] < a.num_blocks) p.x = ra[i];
+      if (2 * tile + 1 < nl[i] && rb[i] >= 0 && rb[i] < a.num_blocks) p.y = rb[i];
+      pr[m0 + i][tid] = p;
+    }
   }
   // first occurrences of each distinct pair (a column of pr is this thread's alone)
   uint32_t first = 0;
@@ -412,13 +422,16 @@ __global__ __launch_bounds__(256, 2) void gqa_decode_kernel(GqaDecodeArgs a) {
 
     // ---- merge the 4 wave states pairwise in a fixed order: (w0+w2) + (w1+w3)
     l_run += __shfl_xor(l_run, 32);
-    float* buf = reinterpret_cast<float*>(&sm.v[0][0]);   // [2][32 rows][D] floats
+    // [2 slots][32 rows][D + 4] floats: the 16-byte row pad puts the 32 rows of one 16-byte
+  // column in distinct LDS banks
+  float* buf = reinterpret_cast<float*>(&sm.v[0][0]);
+  static_assert(2 * 32 * (D + 4) * 4 <= sizeof(sm.v), "merge slots fit in the V slices");
     auto put = [&](int slot) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<f32x4*>(buf + ((size_t)slot * 32 + c32) * D + 32 * mt + 8 * q4 + 4 * h32) =
+          *reinterpret_cast<f32x4*>(buf + ((size_t)slot * 32 + c32) * (D + 4) + 32 * mt + 8 * q4 + 4 * h32) =
               f32x4{acc[mt][4 * q4], acc[mt][4 * q4 + 1], acc[mt][4 * q4 + 2], acc[mt][4 * q4 + 3]};
       if (h32 == 0) { mrg_ml[slot][0][c32] = m_run; mrg_ml[slot][1][c32] = l_run; }
     };
@@ -431,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void gqa_decode_kernel(GqaDecodeArgs a) {
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 o = *reinterpret_cast<const f32x4*>(buf + ((size_t)slot * 32 + c32) * D + 32 * mt + 8 * q4 + 4 * h32);
+          const f32x4 o = *reinterpret_cast<const f32x4*>(buf + ((size_t)slot * 32 + c32) * (D + 4) + 32 * mt + 8 * q4 + 4 * h32);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[mt][4 * q4 + i] = acc[mt][4 * q4 + i] * sa + o[i] * sb;
         }

@@ -52,15 +52,35 @@ static_assert(kKS >= kDqk + 16, "row 0's padding takes the discarded chunk slots
 template <int N>
 using Int = std::integral_constant<int, N>;
 
-__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+// LDS-DMA of 16 (or 4) bytes per lane: lane l's global bytes land at LDS byte address
+// lds_dst + 16 l (4 l); lds_dst must be the same for every lane.  Issued as inline assembly, so the compiler
+// does not track these LDS writes: it would otherwise wait for every outstanding DMA
+// before any LDS read it cannot prove disjoint (the S exchange and the transpose reads
+// among them), draining the pipeline.  The pipeline waits explicitly (wait_vm0, then a
+// barrier) before any wave reads what a DMA wrote.  M0 holds the LDS base; nothing else
+// in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_dst) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(l) : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 4, 0, 0);
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds_dst) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(l) : "memory", "m0");
 }
+// LDS byte address of a pointer into a __shared__ object.
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+#pragma clang diagnostic pop
 // Wait until no vector-memory operation of this wave is outstanding (gfx9 s_waitcnt
 // encoding: vmcnt 0, expcnt and lgkmcnt left at their maxima).
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+// (also a compiler barrier: no LDS read of DMA data moves above it)
+__device__ __forceinline__ void wait_vm0() {
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
 // Workgroup barrier that orders LDS accesses only.  A full __syncthreads() also waits for
 // outstanding vector-memory operations -- here the LDS-DMA of a later tile, still in
 // flight on purpose.
@@ -106,7 +126,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
   __shared__ int32_t bt_s[SPARSE ? (STAGED ? kBtLds : 1) : kDecodeSplitMla / kBs + 1];
   __shared__ int32_t sel_s[SPARSE && STAGED ? kSelLds : 1];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keep it scalar
   const int l32 = lane & 31, h = lane >> 5;
   const int grp32 = wave / SPLIT;                    // which 32 rows
   const int half = wave % SPLIT;                     // which share of the dims
@@ -220,10 +241,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
 #pragma unroll
       for (int m = 0; m < kLoadsPerWave; ++m) {
         const int j = wave + NW * m;
-        if (j < kWaveLoads) dma16(pb >= 0 ? span + 16 * (64 * j + ln) : kv, R + 1024 * j);
+        if (j < kWaveLoads) dma16(pb >= 0 ? span + 16 * (64 * j + ln) : kv, lds_u32(R) + 1024 * j);
       }
       if (wave == NW - 1 && ln < kKT) {
-        dma4(pb >= 0 ? kv_scale + (size_t)pb * kBs + pos0 % kBs + ln : kv_scale, RS);
+        dma4(pb >= 0 ? kv_scale + (size_t)pb * kBs + pos0 % kBs + ln : kv_scale, lds_u32(RS));
         RK[ln] = (pb >= 0 && kb + ln < n_keys) ? pos0 + ln : -1;
       }
     } else {
@@ -239,12 +260,12 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
         const int j = wave + NW * m;
         const int dc = (64 * j + ln) % (kDqk / 16);
         if (j < kWaveLoads)
-          dma16(pbk[m] >= 0 ? kv + ((size_t)pbk[m] * kBs + idx[m] % kBs) * kDqk + 16 * dc : kv, R + 1024 * j);
+          dma16(pbk[m] >= 0 ? kv + ((size_t)pbk[m] * kBs + idx[m] % kBs) * kDqk + 16 * dc : kv, lds_u32(R) + 1024 * j);
       }
       if (wave == NW - 1 && ln < kKT) {
         int id;
         const int pb = key_loc(kb + ln, id);
-        dma4(pb >= 0 ? kv_scale + (size_t)pb * kBs + id % kBs : kv_scale, RS);
+        dma4(pb >= 0 ? kv_scale + (size_t)pb * kBs + id % kBs : kv_scale, lds_u32(RS));
         RK[ln] = pb >= 0 ? id : -1;
       }
     }
