@@ -61,7 +61,11 @@ GqaDecodeDims gqa_decode_dims(int num_seqs, int q_per_seq, int num_q_heads, int 
 
 namespace {
 
-constexpr int kWaves = 4;
+// Waves per attention workgroup; 8 / kWaves workgroups share a compute unit.
+constexpr int kWaves = PA_DECODE_WAVES;
+constexpr int kThreads = 64 * kWaves;
+static_assert(kWaves == 2 || kWaves == 4 || kWaves == 8, "waves per workgroup");
+static_assert(kUnitPasses <= kThreads, "a unit's descriptors are staged one per thread");
 constexpr int kTile = 32;               // keys per pass (two 16-token blocks)
 
 // ---------------------------------------------------------------------------------
@@ -217,14 +221,14 @@ struct Pass {
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void gqa_decode_kernel(GqaDecodeArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gqa_decode_kernel(GqaDecodeArgs a) {
   constexpr int KS = D / 16;   // QK k-steps (32x32x16)
   constexpr int MT = D / 32;   // O^T tiles of 32 dims
   constexpr int DC = D / 8;    // 16-byte chunks per V row
   constexpr int VG = D / 64;   // (4 keys x 8 dims) V groups per lane per pass
   using Sm = DecodeSmem<D>;
   __shared__ __attribute__((aligned(16))) Sm sm;
-  __shared__ float mrg_ml[2][2][32];
+  __shared__ float mrg_ml[kWaves / 2][2][32];
   __shared__ int item_s;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(256, 2) void gqa_decode_kernel(GqaDecodeArgs a) {
 
     // ---- the unit's pass descriptors and the group's 32 query rows -> LDS
     if (tid < np) sm.desc[tid] = ld16(a.passes + ((size_t)p_begin + tid) * 4);
-    for (int c = tid; c < 32 * DC; c += 256) {
+    for (int c = tid; c < 32 * DC; c += kThreads) {
       const int r = c / DC, dc = c % DC;
       const int mr = r / R, rr2 = r % R, sr = s0 + mr;
       u32x4 v = {0, 0, 0, 0};
@@ -425,7 +429,7 @@ __global__ __launch_bounds__(256, 2) void gqa_decode_kernel(GqaDecodeArgs a) {
     // [2 slots][32 rows][D + 4] floats: the 16-byte row pad puts the 32 rows of one 16-byte
   // column in distinct LDS banks
   float* buf = reinterpret_cast<float*>(&sm.v[0][0]);
-  static_assert(2 * 32 * (D + 4) * 4 <= sizeof(sm.v), "merge slots fit in the V slices");
+  static_assert(kWaves / 2 * 32 * (D + 4) * 4 <= sizeof(sm.v), "merge slots fit in the V slices");
     auto put = [&](int slot) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -451,15 +455,15 @@ __global__ __launch_bounds__(256, 2) void gqa_decode_kernel(GqaDecodeArgs a) {
       l_run = l_run * sa + lo * sb;
       m_run = Mx;
     };
-    __syncthreads();
-    if (wave >= 2) put(wave - 2);
-    __syncthreads();
-    if (wave < 2) take(wave);
-    __syncthreads();
-    if (wave == 1) put(0);
-    __syncthreads();
+    // tree: waves [h, 2h) hand their state to waves [0, h), h = kWaves/2 .. 1
+#pragma unroll
+    for (int h = kWaves / 2; h >= 1; h /= 2) {
+      __syncthreads();
+      if (wave >= h && wave < 2 * h) put(wave - h);
+      __syncthreads();
+      if (wave < h) take(wave);
+    }
     if (wave == 0) {
-      take(0);
       // every row is written (rows of members outside the unit get lse = -inf); the
       // combine reads only the rows of real sequences
       const size_t pidx = (size_t)item * 32 + c32;
@@ -476,7 +480,7 @@ __global__ __launch_bounds__(256, 2) void gqa_decode_kernel(GqaDecodeArgs a) {
   }  // work items
 }
 
-// Resident workgroups of the persistent decode grid: two per compute unit.
+// Resident workgroups of the persistent decode grid: 8 / kWaves per compute unit.
 int decode_grid(int units_cap, int num_kv_heads) {
   static int cus[64] = {0};
   int dev = 0;
@@ -487,7 +491,7 @@ int decode_grid(int units_cap, int num_kv_heads) {
     cus[dev] = n;
   }
   const long items = (long)units_cap * num_kv_heads;
-  return (int)std::min<long>(items, 2L * cus[dev]);
+  return (int)std::min<long>(items, (long)(8 / kWaves) * cus[dev]);
 }
 
 }  // namespace
@@ -504,9 +508,9 @@ hipError_t launch_gqa_decode(const GqaDecodeArgs& a, hipStream_t stream) {
   if (a.dims.n_groups == 0 || a.dims.n_chunks == 0) return hipSuccess;
   const int grid = decode_grid(a.dims.units_cap, a.num_kv_heads);
   if (a.head_dim == 128)
-    hipLaunchKernelGGL((gqa_decode_kernel<128>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((gqa_decode_kernel<128>), dim3(grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((gqa_decode_kernel<64>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((gqa_decode_kernel<64>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -16,8 +16,11 @@ constexpr int kDecodeSplitMla = PA_DECODE_SPLIT_MLA;
 // GQA decode work units: a group's list of distinct block-pair passes is cut into units
 // of at most kUnitPasses passes (one partial (o, lse) per unit and KV head); the plan
 // covers kPlanTiles 32-key tiles per workgroup.
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 8
+#endif
 #ifndef PA_DECODE_UNIT_PASSES
-#define PA_DECODE_UNIT_PASSES 64
+#define PA_DECODE_UNIT_PASSES (16 * PA_DECODE_WAVES)
 #endif
 constexpr int kUnitPasses = PA_DECODE_UNIT_PASSES;
 constexpr int kPlanTiles = 256;
