@@ -155,18 +155,24 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
         sacc[st] = mfma32x32x16(*reinterpret_cast<const u32x4*>(kp + 16 * ks), qb[ks], sacc[st]);
     }
     // ---- causal mask (diagonal tiles only) and the row maximum on raw scores
-    const bool need_mask = kt + kKT - 1 > wave_min_pos;
     float mx = -INFINITY;
+    if (kt + kKT - 1 > wave_min_pos) {
+      // register i of sub-tile st holds key kt + 32 st + 4 h32 + 8 (i/4) + i%4
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st) {
+        const int lim = pos - kt - 32 * st - 4 * h32;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (need_mask) {
-          const int key = kt + 32 * st + 8 * (i >> 2) + 4 * h32 + (i & 3);
-          if (key > pos) sacc[st][i] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          if (8 * (i >> 2) + (i & 3) > lim) sacc[st][i] = -INFINITY;
+          mx = fmaxf(mx, sacc[st][i]);
         }
-        mx = fmaxf(mx, sacc[st][i]);
       }
+    } else {                                     // every key of the tile is visible
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[st][i]);
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
     if (__ballot(mx > m_run + 8.f) != 0) {
       const float m_new = fmaxf(m_run, mx);
