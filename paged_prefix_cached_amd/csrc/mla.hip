@@ -317,15 +317,17 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
     const float* RS = P ? rs1 : rs0;
     const int32_t* RK = P ? rk1 : rk0;
     if (wave == 0) {
-      const int id = lane < kKT ? RK[lane] : 0;
-      const float sc = lane < kKT ? RS[lane] : 0.f;
-      if (lane < kKT) {
-        fk[P][lane] = id;
-        fks[P][lane] = id >= 0 ? sc * scale_log2 : 0.f;
-        fvs[P][lane] = id >= 0 ? sc : 0.f;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));   // recompute the addresses here, keep no VGPRs for them
+      const int id = ln < kKT ? RK[ln] : 0;
+      const float sc = ln < kKT ? RS[ln] : 0.f;
+      if (ln < kKT) {
+        fk[P][ln] = id;
+        fks[P][ln] = id >= 0 ? sc * scale_log2 : 0.f;
+        fvs[P][ln] = id >= 0 ? sc : 0.f;
       }
       const bool all_valid = __ballot(id < 0) == 0;
-      if (lane == 0) fall[P] = all_valid ? 1 : 0;
+      if (ln == 0) fall[P] = all_valid ? 1 : 0;
     }
   };
   auto convert = [&](auto P) {
