@@ -15,10 +15,16 @@ textbook reading of the named operation.
 Pins (tests/test_oracle_*.py) tie each function to something other than itself:
 brute-force loops with math.fsum, closed forms, invariants, permuted block tables,
 special cases (k >= context => dense; GQA == MHA with repeated KV), the OCP E4M3 table.
+The KV append (append.py) quantises each new token to FP8 by a nearest-value search over
+the E4M3 table; that encoder is pinned to the format's halfway points and saturation, to
+the round trip of every code and to PyTorch's own float8_e4m3fn conversion.
 No function here is "parity unpinned".
 """
 from .formats import bf16_to_f64, e4m3_decode  # noqa: F401
 from .attention import (  # noqa: F401
     gather_paged, attention, attention_probs, lse_merge, paged_gqa_attention,
     mla_dequant, mla_attention, indexer_scores, topk_indices, sparse_mla_attention,
+)
+from .append import (  # noqa: F401
+    e4m3_nearest, quantize_token_fp8, token_positions, append_gqa, append_fp8,
 )
