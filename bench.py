@@ -280,6 +280,65 @@ def bench_sparse(steps, warmup):
     return out
 
 
+def bench_append(steps, warmup):
+    """paged_kv_append on the three workloads' new tokens, into pools of their full size:
+    the suffix prefill (8 x 2048 rows of 8 KV heads x 128, bf16 K and V), the MLA MTP3
+    decode step (64 x 4 latent rows) and the sparse-MLA prefill (4096 latent rows plus
+    4096 indexer-key rows), the FP8 rows quantised per token.  Algorithmic bytes: input
+    rows read once, pool rows (and scales) written once."""
+    import torch
+    import paged_prefix_cached_amd as pa
+    import workloads as W
+    from workloads.device import t as to_dev
+    g = torch.Generator(device="cuda")
+    g.manual_seed(80)
+
+    def layout(seed, cached, new, bs):
+        a = W.make_append(seed, cached=cached, new=new, block_size=bs, row_shape=(1,), with_v=False)
+        return a, [to_dev(x, "cuda") for x in (a.block_table, a.cached_len, a.new_len, a.q_start)]
+
+    def rows(n, *shape):
+        return torch.randn((n,) + shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+    a3, d3 = layout(81, [142000] * 8, [2048] * 8, 16)
+    kp = torch.empty((a3.num_blocks, 8, 16, 128), dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty_like(kp)
+    gqa = pa.gqa_pool(kp, vp)
+    k3, v3 = rows(16384, 8, 128), rows(16384, 8, 128)
+    ctx = np.random.default_rng(82).integers(32768, 262145, 64)
+    a4, d4 = layout(82, ctx - 4, [4] * 64, 64)
+    p4 = torch.empty((a4.num_blocks, 64, 576), dtype=torch.uint8, device="cuda")
+    s4 = torch.empty((a4.num_blocks, 64), dtype=torch.float32, device="cuda")
+    mla4 = pa.mla_pool(p4, s4)
+    x4 = rows(256, 576)
+    a5, d5 = layout(83, [131072], [4096], 64)
+    p5 = torch.empty((a5.num_blocks, 64, 576), dtype=torch.uint8, device="cuda")
+    s5 = torch.empty((a5.num_blocks, 64), dtype=torch.float32, device="cuda")
+    i5 = torch.empty((a5.num_blocks, 64, 128), dtype=torch.uint8, device="cuda")
+    is5 = torch.empty((a5.num_blocks, 64), dtype=torch.float32, device="cuda")
+    mla5, idx5 = pa.mla_pool(p5, s5), pa.indexer_pool(i5, is5)
+    x5, xi5 = rows(4096, 576), rows(4096, 128)
+    torch.cuda.synchronize()
+
+    def step():
+        pa.paged_kv_append(gqa, *d3, k3, v3, max_new_len=2048)
+        pa.paged_kv_append(mla4, *d4, x4, max_new_len=4)
+        pa.paged_kv_append(mla5, *d5, x5, max_new_len=4096)
+        pa.paged_kv_append(idx5, *d5, xi5, max_new_len=4096)
+
+    ms, kern = timed_steps(step, steps, warmup)
+    gqa_bytes = 2 * (16384 * 8 * 128 * 2 * 2)
+    fp8_bytes = 256 * (576 * 3 + 4) + 4096 * (576 * 3 + 4) + 4096 * (128 * 3 + 4)
+    k_ms = kern.get("append_gqa", float("nan"))
+    ach = gqa_bytes / (k_ms * 1e-3) / 1e9
+    return {"workload": "KV append: 8 x 2048 bf16 rows (8 KV heads x 128) + 64 x 4 and 4096 FP8 latent "
+                        "rows (576) + 4096 FP8 indexer rows (128), per-token quantisation",
+            "ms": ms, "kernel_ms": kern, "bytes": gqa_bytes + fp8_bytes,
+            "gbps": (gqa_bytes + fp8_bytes) / (ms * 1e-3) / 1e9,
+            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": ach / HBM_PEAK_GBS, "kernel": "append_gqa_kernel"}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,7 +346,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--secondary", default="", help="comma list of extra workloads: 2n (decode with no "
                                                     "shared blocks), 3 (prefill), 4 (MLA MTP3 decode), "
-                                                    "5 (indexer + sparse MLA)")
+                                                    "5 (indexer + sparse MLA), a (KV append)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (reference kernel for HBM counters)")
@@ -326,7 +385,7 @@ def main():
                                                               "tokens_per_s", "kernel_ms", "roofline")}
                 continue
             f = {"3": ("prefill_suffix", bench_prefill), "4": ("mla_decode_mtp3", bench_mla),
-                 "5": ("indexer_topk_sparse_mla", bench_sparse)}[c]
+                 "5": ("indexer_topk_sparse_mla", bench_sparse), "a": ("kv_append", bench_append)}[c]
             sec[f[0]] = f[1](max(2, args.steps // 4), max(1, args.warmup // 2))
             torch.cuda.empty_cache()
         line["secondary"] = sec

@@ -1,7 +1,7 @@
 /*
  * pa.h -- paged, prefix-reused attention for AMD MI355X (gfx950).  C ABI.
  *
- * Four calls make up the hot path of agentic serving as the pages describe it: new
+ * Five calls make up the hot path of agentic serving as the pages describe it: new
  * query tokens attend to a paged KV cache whose long prefix is reused across turns.
  *
  *   paged_attn_prefill   suffix prefill on top of a cached prefix (GQA / MHA, bf16)
@@ -9,6 +9,8 @@
  *                        FP8 MLA latent cache shared by all query heads)
  *   mla_indexer_topk     indexer scores plus per-query top-k (k = 2048 in the pages)
  *   sparse_mla_attn      MLA attention restricted to the selected tokens
+ *   paged_kv_append      writes the new tokens' K/V into the pool (FP8 pools quantised
+ *                        per token)
  *
  * Sources (page title, section):
  *   [AgentX] vLLM AgentX article (news.ainew.jp):
@@ -210,6 +212,43 @@ pa_status sparse_mla_attn(const void* q, const pa_kv_pool* pool, const int32_t* 
                           hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
+ * 5. Paged KV append with per-token FP8 quantisation ([AgentX] "Hybrid KV cache
+ *    management": the new tokens' KV goes into blocks of the one shared pool through the
+ *    block table; [GLM] "Configuration and numbers" table: FP8 KV; "What's new": one
+ *    latent row per token, shared by the query heads).
+ *
+ * New token j < new_len[s] of sequence s is input row q_start[s] + j and is written to
+ * logical position cached_len[s] + j, i.e. row (cached_len[s]+j) % block_size of block
+ * block_table[s*bt_stride + (cached_len[s]+j)/block_size].  Nothing else in the pool
+ * changes.  This is the call that fills the pool before prefill (cached_len = prefix
+ * length) or decode (cached_len = context_len - q_per_seq).
+ *   pool    GQA bf16 pool: k_new, v_new dev bf16 [n_tokens][num_kv_heads][head_dim] are
+ *           copied bit for bit.
+ *           FP8 pools (MLA latent 576 or indexer keys 128): k_new dev bf16
+ *           [n_tokens][head_dim_qk], v_new ignored.  Each row x is quantised on its
+ *           own: scale = amax/448 with amax = max|x| (scale = 1 for an all-zero row),
+ *           code[e] = OCP E4M3 round-to-nearest-even of x[e]/scale, both divisions IEEE
+ *           float32, magnitudes past 448 clamped to 448; pool->scale gets the scale.
+ *           The pages print no quantiser: this per-token amax scaling is the plain one.
+ *           pool->k, pool->v and pool->scale must point to writable device memory.
+ *   block_table dev int32 [num_seqs][bt_stride]; cached_len, new_len, q_start dev int32
+ *           [num_seqs].
+ *   n_tokens     number of input rows; rows outside [0, n_tokens) are never read.
+ *   max_new_len  host upper bound of new_len[s] (grid sizing; larger values are clamped).
+ * Tokens whose position falls outside the block table's bt_stride entries, or whose
+ * block id is out of range, are not written.  The destination rows of different
+ * sequences must be distinct (prefix-shared blocks are full and never appended to); if
+ * two tokens map to one row, which one lands is unspecified.  Inputs must be finite.
+ * Supported: the GQA pool of call 1 and the FP8 MLA / indexer pools; num_seqs <= 65535.
+ * No workspace.
+ * ------------------------------------------------------------------------------- */
+pa_status paged_kv_append(const pa_kv_pool* pool, const int32_t* block_table, int32_t bt_stride,
+                          const int32_t* cached_len, const int32_t* new_len,
+                          const int32_t* q_start, int32_t num_seqs, int32_t n_tokens,
+                          int32_t max_new_len, const void* k_new, const void* v_new,
+                          hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
  * Test hooks (not part of the serving API).
  *
  * pa_test_gather_kv: copies the first n_tokens logical tokens of sequence `seq` out of
@@ -239,7 +278,7 @@ pa_status pa_test_topk_from_scores(const float* scores, const int32_t* valid_len
  * pa_profile_count(): number of launches recorded so far.
  * pa_profile_record(i, name, cap, ms): waits for record i and returns its kernel name
  *   ("prefill_gqa", "decode_gqa", "decode_mla", "combine", "indexer", "topk",
- *   "sparse_mla") and its duration in milliseconds.
+ *   "sparse_mla", "append_gqa", "append_fp8") and its duration in milliseconds.
  * pa_profile_disable(): stops recording and destroys the events.
  * ------------------------------------------------------------------------------- */
 pa_status pa_profile_enable(int32_t max_records);

@@ -6,7 +6,8 @@ stream.  There is no CPU or Python fallback: if the library is missing or a call
 an exception is raised.
 
 Functions (same names as the C entry points):
-    paged_attn_prefill, paged_attn_decode, mla_indexer_topk, sparse_mla_attn
+    paged_attn_prefill, paged_attn_decode, mla_indexer_topk, sparse_mla_attn,
+    paged_kv_append
 Pool descriptors:
     gqa_pool(k_pool, v_pool), mla_pool(kv_pool, kv_scale), indexer_pool(keys, scale)
 Test hooks:
@@ -19,7 +20,7 @@ import os
 
 __all__ = ["load", "PAError", "KVPool", "gqa_pool", "mla_pool", "indexer_pool",
            "paged_attn_prefill", "paged_attn_decode", "mla_indexer_topk", "sparse_mla_attn",
-           "pa_test_gather_kv", "pa_test_topk_from_scores", "pa_profile_enable",
+           "paged_kv_append", "pa_test_gather_kv", "pa_test_topk_from_scores", "pa_profile_enable",
            "pa_profile_records", "pa_profile_disable", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
@@ -55,6 +56,8 @@ _SIGS = {
     "sparse_mla_attn_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32]),
     "sparse_mla_attn": (_c_i32, [_vp, _vp, _vp, _c_i32, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_f,
                                  _vp, _vp, _vp, _c_sz, _vp]),
+    "paged_kv_append": (_c_i32, [_vp, _vp, _c_i32, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _vp,
+                                 _vp, _vp]),
     "pa_test_gather_kv": (_c_i32, [_vp, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp]),
     "pa_test_topk_workspace_size": (_c_sz, [_c_i32, _c_i32]),
     "pa_test_topk_from_scores": (_c_i32, [_vp, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, _vp]),
@@ -205,6 +208,20 @@ def sparse_mla_attn(q, pool: KVPool, block_table, q_seq, topk_idx, *, scale: flo
                                _p(q_seq), _p(topk_idx), n_q, k, Hq, scale, _p(out), _p(lse), None, 0,
                                _stream(q)), "sparse_mla_attn")
     return out
+
+
+def paged_kv_append(pool: KVPool, block_table, cached_len, new_len, q_start, k_new, v_new=None,
+                    *, max_new_len: int):
+    """Write the new rows k_new (and v_new for a bf16 pool) into the pool in place.
+
+    GQA: k_new, v_new [n_tokens][num_kv_heads][head_dim] bf16.  FP8 pools (MLA latent or
+    indexer keys): k_new [n_tokens][head_dim_qk] bf16, quantised per token on the GPU; the
+    pool's bytes and scales are updated."""
+    lib = load()
+    _check(lib.paged_kv_append(ctypes.byref(pool), _p(block_table), block_table.shape[1],
+                               _p(cached_len), _p(new_len), _p(q_start), block_table.shape[0],
+                               k_new.shape[0], max_new_len, _p(k_new), _p(v_new),
+                               _stream(k_new)), "paged_kv_append")
 
 
 def pa_profile_enable(max_records: int) -> None:

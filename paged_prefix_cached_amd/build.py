@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libpa.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["pa_abi.cpp", "gather.hip", "prefill_gqa.hip", "decode_gqa.hip", "mla.hip",
-           "indexer.hip", "topk.hip"]
+           "indexer.hip", "topk.hip", "append.hip"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}", "-Wall",

@@ -1,0 +1,141 @@
+// Paged KV append: the new tokens of a step are written into their sequences' blocks,
+// bf16 rows copied as they are, FP8 rows quantised per token.
+//
+// Sources: vLLM AgentX article (news.ainew.jp), "Hybrid KV cache management" -- one
+// shared block pool, logical token t of a sequence in row t % block_size of physical
+// block block_table[t / block_size], so an append is a scatter through the table.
+// GLM-5.3 on 16xH200 report (aisoku.org), "Configuration and numbers" table (FP8 KV) and
+// "What's new" (one latent KV row per token) -- the cache holds FP8.  The pages give no
+// quantiser; the one here is per token: scale = amax / 448 (1 when the row is all zero),
+// code = E4M3 round-to-nearest-even of x / scale in IEEE float32, clamped to +-448.
+//
+// Both kernels are grids of (token range, sequence); a sequence's rows are q_start[s] ..
+// q_start[s] + new_len[s] - 1 of the packed input and go to logical positions
+// cached_len[s] ... .  The work is pure HBM streaming: each input byte is read once and
+// each pool byte written once, in 16-byte (bf16) or 8-byte (FP8) vector accesses.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kGqaTokensPerBlock = 4;
+constexpr int kFp8WavesPerBlock = 4;   // one token per wave
+
+// Pool row of new token j of sequence s, or -1 when it has none (outside the input
+// rows, outside the block table, or an out-of-range block id).  *row_out gets the input
+// row.
+__device__ __forceinline__ long dest_slot(const AppendArgs& a, int s, int j, int* row_out) {
+  const int nl = min(a.new_len[s], a.max_new_len);
+  if (j >= nl) return -1;
+  const int row = a.q_start[s] + j;
+  if (row < 0 || row >= a.n_tokens) return -1;
+  const int pos = a.cached_len[s] + j;
+  if (pos < 0) return -1;
+  const int lb = pos / a.block_size;
+  if (lb >= a.bt_stride) return -1;
+  const int b = a.bt[(size_t)s * a.bt_stride + lb];
+  if (b < 0 || b >= a.num_blocks) return -1;
+  *row_out = row;
+  return (long)b * a.block_size + pos % a.block_size;
+}
+
+// bf16 GQA pool [NB][Hkv][bs][d]: one thread per 16-byte chunk of K or V.
+__global__ __launch_bounds__(256) void append_gqa_kernel(AppendArgs a) {
+  const int s = blockIdx.y;
+  const int chunks = a.head_dim / 8;                 // 16-byte chunks per head row
+  const int per_tok = a.num_kv_heads * chunks;       // chunks of one token's K (or V)
+  const int j0 = blockIdx.x * kGqaTokensPerBlock;
+  for (int idx = threadIdx.x; idx < kGqaTokensPerBlock * 2 * per_tok; idx += blockDim.x) {
+    const int t = idx / (2 * per_tok);
+    const int r = idx - t * 2 * per_tok;
+    const int kv = r >= per_tok;
+    const int hc = r - kv * per_tok;                 // head * chunks + chunk
+    int row;
+    const long slot = dest_slot(a, s, j0 + t, &row);
+    if (slot < 0) continue;
+    const int h = hc / chunks, c = hc - h * chunks;
+    const long blk = slot / a.block_size, rr = slot - blk * a.block_size;
+    const uint16_t* src = (kv ? a.v_new : a.k_new) + ((size_t)row * a.num_kv_heads * a.head_dim) + 8 * hc;
+    uint16_t* dst = (kv ? a.v_out : a.k_out) +
+                    (((size_t)blk * a.num_kv_heads + h) * a.block_size + rr) * a.head_dim + 8 * c;
+    st16(dst, ld16(src));
+  }
+}
+
+// FP8 pool [NB][bs][D] + scales [NB][bs]: one wave per token.  Lane l holds the 8-element
+// chunks l, l + 64, ... of the row in registers (D <= 1024), so the row is read once.
+template <int D>
+__global__ __launch_bounds__(64 * kFp8WavesPerBlock) void append_fp8_kernel(AppendArgs a) {
+  constexpr int kChunks = D / 8;
+  constexpr int kPer = (kChunks + 63) / 64;
+  const int s = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * kFp8WavesPerBlock + (threadIdx.x >> 6);
+  int row;
+  const long slot = dest_slot(a, s, j, &row);
+  if (slot < 0) return;                              // the whole wave agrees
+  const uint16_t* src = a.k_new + (size_t)row * D;
+  float x[kPer][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = lane + 64 * i;
+    u32x4 v = {0, 0, 0, 0};
+    if (c < kChunks) v = ld16(src + 8 * c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[i][2 * e] = __uint_as_float(w[e] << 16);
+      x[i][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      amax = fmaxf(amax, fmaxf(fabsf(x[i][2 * e]), fabsf(x[i][2 * e + 1])));
+    }
+  }
+  amax = wave_max_xor(amax, 64);
+  // IEEE float32 division (correctly rounded): the code of every element is decided on
+  // exactly the value x / scale.
+  const float scale = amax > 0.f ? amax / 448.f : 1.f;
+  uint8_t* dst = a.fp8_out + slot * D;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= kChunks) continue;
+    uint32_t packed[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf(x[i][4 * h + e] / scale, -448.f), 448.f);
+      int p = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      p = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], p, true);
+      packed[h] = (uint32_t)p;
+    }
+    u32x2 o;
+    o.x = packed[0];
+    o.y = packed[1];
+    *reinterpret_cast<u32x2*>(dst + 8 * c) = o;
+  }
+  if (lane == 0) a.scale_out[slot] = scale;
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
+  if (a.num_seqs == 0 || a.max_new_len == 0) return hipSuccess;
+  if (!a.is_fp8) {
+    const dim3 grid((a.max_new_len + kGqaTokensPerBlock - 1) / kGqaTokensPerBlock, a.num_seqs);
+    hipLaunchKernelGGL(append_gqa_kernel, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  const dim3 grid((a.max_new_len + kFp8WavesPerBlock - 1) / kFp8WavesPerBlock, a.num_seqs);
+  const dim3 block(64 * kFp8WavesPerBlock);
+  if (a.head_dim == 576)
+    hipLaunchKernelGGL(append_fp8_kernel<576>, grid, block, 0, stream, a);
+  else if (a.head_dim == 128)
+    hipLaunchKernelGGL(append_fp8_kernel<128>, grid, block, 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pa

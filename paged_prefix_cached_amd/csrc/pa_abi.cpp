@@ -440,6 +440,62 @@ pa_status sparse_mla_attn(const void* q, const pa_kv_pool* pool, const int32_t* 
   return launched(timed("sparse_mla", stream, [&] { return pa::launch_sparse_mla(a, stream); }), "sparse MLA launch");
 }
 
+// ------------------------------------------------------------------------- KV append
+pa_status paged_kv_append(const pa_kv_pool* pool, const int32_t* block_table, int32_t bt_stride,
+                          const int32_t* cached_len, const int32_t* new_len, const int32_t* q_start,
+                          int32_t num_seqs, int32_t n_tokens, int32_t max_new_len, const void* k_new,
+                          const void* v_new, hipStream_t stream) {
+  g_detail[0] = 0;
+  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+  const bool fp8 = pool->kv_dtype == PA_FP8_E4M3;
+  if (fp8) {
+    if (pool->head_dim_qk == 576)
+      PA_TRY(check_fp8_pool(pool, 576, 512, "MLA"));
+    else
+      PA_TRY(check_fp8_pool(pool, 128, 0, "indexer"));
+  } else {
+    PA_TRY(check_gqa_pool(pool));
+    if (v_new == nullptr) return fail(PA_ERR_INVALID_ARG, "v_new is NULL for a bf16 pool");
+    if (!aligned(v_new, 16)) return fail(PA_ERR_INVALID_ARG, "v_new must be 16-byte aligned");
+  }
+  if (num_seqs < 0 || n_tokens < 0 || max_new_len < 0) return fail(PA_ERR_INVALID_ARG, "negative size");
+  if (num_seqs == 0 || n_tokens == 0 || max_new_len == 0) return PA_OK;
+  if (bt_stride < 1) return fail(PA_ERR_INVALID_ARG, "bt_stride must be >= 1");
+  if (block_table == nullptr || cached_len == nullptr || new_len == nullptr || q_start == nullptr ||
+      k_new == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(k_new, 16)) return fail(PA_ERR_INVALID_ARG, "k_new must be 16-byte aligned");
+  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs must be <= 65535");
+  (void)hipGetLastError();
+  pa::AppendArgs a{};
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.bt = block_table;
+  a.cached_len = cached_len;
+  a.new_len = new_len;
+  a.q_start = q_start;
+  // the pool descriptor's pointers are const for the attention calls; the append is the
+  // one call that writes through them
+  if (fp8) {
+    a.fp8_out = static_cast<uint8_t*>(const_cast<void*>(pool->k));
+    a.scale_out = const_cast<float*>(pool->scale);
+  } else {
+    a.k_out = static_cast<uint16_t*>(const_cast<void*>(pool->k));
+    a.v_out = static_cast<uint16_t*>(const_cast<void*>(pool->v));
+  }
+  a.bt_stride = bt_stride;
+  a.num_seqs = num_seqs;
+  a.n_tokens = n_tokens;
+  a.max_new_len = max_new_len;
+  a.num_blocks = pool->num_blocks;
+  a.block_size = pool->block_size;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim_qk;
+  a.is_fp8 = fp8 ? 1 : 0;
+  return launched(timed(fp8 ? "append_fp8" : "append_gqa", stream, [&] { return pa::launch_append(a, stream); }),
+                  "append launch");
+}
+
 // ------------------------------------------------------------------------- test hooks
 pa_status pa_test_gather_kv(const pa_kv_pool* pool, const int32_t* block_table, int32_t bt_stride,
                             int32_t seq, int32_t n_tokens, void* k_out, void* v_out,

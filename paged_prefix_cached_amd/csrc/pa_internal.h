@@ -143,6 +143,22 @@ struct GatherArgs {
   int32_t is_fp8;
 };
 
+struct AppendArgs {
+  const uint16_t* k_new;        // bf16 [n_tokens][Hkv][d] (GQA) or [n_tokens][D] (FP8 pools)
+  const uint16_t* v_new;        // bf16 [n_tokens][Hkv][d] (GQA) or null
+  const int32_t* bt;
+  const int32_t* cached_len;
+  const int32_t* new_len;
+  const int32_t* q_start;
+  uint16_t* k_out;              // GQA pool K / V [NB][Hkv][bs][d]
+  uint16_t* v_out;
+  uint8_t* fp8_out;             // FP8 pool [NB][bs][D]
+  float* scale_out;             // [NB][bs]
+  int32_t bt_stride, num_seqs, n_tokens, max_new_len, num_blocks, block_size, num_kv_heads;
+  int32_t head_dim;             // d (GQA) or D (FP8)
+  int32_t is_fp8;
+};
+
 hipError_t launch_gqa_prefill(const GqaPrefillArgs& a, hipStream_t s);
 // GQA decode = plan (pass lists, units, queue reset) then the persistent attention grid.
 hipError_t launch_gqa_decode_plan(const GqaDecodeArgs& a, hipStream_t s);
@@ -153,5 +169,6 @@ hipError_t launch_sparse_mla(const SparseMlaArgs& a, hipStream_t s);
 hipError_t launch_indexer_scores(const IndexerArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 
 }  // namespace pa

@@ -31,7 +31,7 @@ __all__ = [
     "BF16_NAN", "FP8_NAN", "bf16_bits", "bf16_bits_to_f32", "e4m3_encode",
     "fp8_quantize_tokens", "normal_f32", "PagedGQA", "PagedMLA", "IndexerInput",
     "make_prefill_tiny", "make_gqa_decode", "make_prefix_prefill", "make_mla_decode",
-    "make_sparse_mla", "make_gqa", "tie_scores", "CONFIG_NAMES",
+    "make_sparse_mla", "make_gqa", "tie_scores", "CONFIG_NAMES", "AppendInput", "make_append",
 ]
 
 BF16_NAN = np.uint16(0x7FC0)
@@ -512,3 +512,50 @@ def make_sparse_mla(seed: int = 5, *, cached: int = 131072, new: int = 4096, num
 def tie_scores(seed: int, n_rows: int, n_cols: int, levels: int = 3) -> np.ndarray:
     """Scores drawn from {0, 1, ..., levels-1}: heavy ties for the lower-index rule."""
     return _rng(seed, 11).integers(0, levels, (n_rows, n_cols)).astype(np.float32)
+
+
+# --------------------------------------------------------------------------- KV append
+@dataclass
+class AppendInput:
+    """New KV rows of one step and where they go: sequence s appends new_len[s] rows (input
+    rows q_start[s] ...) after its cached_len[s] tokens.  Every sequence owns distinct
+    blocks (a shuffled pool), so no two rows share a destination."""
+    block_size: int
+    num_blocks: int
+    block_table: np.ndarray        # int32 [S][width], -1 past a sequence's last block
+    cached_len: np.ndarray         # int32 [S]
+    new_len: np.ndarray            # int32 [S]
+    q_start: np.ndarray            # int32 [S]
+    k_new: np.ndarray              # uint16 bf16 bits [n][*row_shape]
+    v_new: np.ndarray | None       # same shape or None (FP8 pools)
+
+
+def make_append(seed: int, *, cached, new, block_size: int, row_shape, with_v: bool,
+                row_mults=(1.0,), zero_rows: int = 0, slack: int = 3) -> AppendInput:
+    """Append layout plus N(0,1) rows; row i is scaled by row_mults[i % len(row_mults)] and
+    the first zero_rows rows are all zero (the degenerate amax = 0 case)."""
+    rng = _rng(seed, 20)
+    cached = np.asarray(cached, np.int64)
+    new = np.asarray(new, np.int64)
+    need = -(-(cached + new) // block_size)
+    width = int(max(1, need.max()))
+    nb = int(need.sum()) + slack
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.full((len(cached), width), -1, np.int32)
+    k = 0
+    for s, m in enumerate(need):
+        bt[s, :m] = perm[k:k + m]
+        k += int(m)
+    q_start = np.concatenate([[0], np.cumsum(new)[:-1]]).astype(np.int32)
+    n = int(new.sum())
+    shape = (n,) + tuple(row_shape)
+    mult = np.asarray(row_mults, np.float32)[np.arange(n) % len(row_mults)]
+    mult = mult.reshape((n,) + (1,) * len(row_shape))
+
+    def rows(stream):
+        x = normal_f32(seed, stream, int(np.prod(shape))).reshape(shape) * mult
+        x[:zero_rows] = 0
+        return _par_map(bf16_bits, x).reshape(shape)
+
+    return AppendInput(block_size, nb, bt, cached.astype(np.int32), new.astype(np.int32), q_start,
+                       rows(21), rows(22) if with_v else None)
