@@ -19,51 +19,81 @@
 namespace pa {
 namespace {
 
-constexpr int kGqaTokensPerBlock = 4;
+constexpr int kGqaTokensPerBlock = 8;
 constexpr int kFp8WavesPerBlock = 4;   // one token per wave
 
-// Pool row of new token j of sequence s, or -1 when it has none (outside the input
-// rows, outside the block table, or an out-of-range block id).  *row_out gets the input
-// row.
-__device__ __forceinline__ long dest_slot(const AppendArgs& a, int s, int j, int* row_out) {
-  const int nl = min(a.new_len[s], a.max_new_len);
-  if (j >= nl) return -1;
-  const int row = a.q_start[s] + j;
-  if (row < 0 || row >= a.n_tokens) return -1;
-  const int pos = a.cached_len[s] + j;
-  if (pos < 0) return -1;
-  const int lb = pos / a.block_size;
-  if (lb >= a.bt_stride) return -1;
-  const int b = a.bt[(size_t)s * a.bt_stride + lb];
-  if (b < 0 || b >= a.num_blocks) return -1;
-  *row_out = row;
-  return (long)b * a.block_size + pos % a.block_size;
+// Where the new tokens of sequence s go.  The three per-sequence values are loaded
+// together; then slot(j) needs one block-table load.
+struct SeqAppend {
+  int nl, q0, c0;
+};
+
+__device__ __forceinline__ SeqAppend seq_append(const AppendArgs& a, int s) {
+  const int nl = a.new_len[s], q0 = a.q_start[s], c0 = a.cached_len[s];
+  return {min(nl, a.max_new_len), q0, c0};
 }
 
-// bf16 GQA pool [NB][Hkv][bs][d]: one thread per 16-byte chunk of K or V.
+// Pool row (block * BS + row) of new token j, given the block id b of its logical block
+// (read by the caller), or -1 when it has none (beyond new_len, an input row outside
+// [0, n_tokens), a position outside the block table, or an out-of-range block id).
+// *row_out gets the input row, 0 when there is none (row 0 exists: n_tokens >= 1), so
+// that a load from it is always in bounds.
+template <int BS>
+__device__ __forceinline__ long dest_slot(const AppendArgs& a, const SeqAppend& q, int j, int b,
+                                          int* row_out) {
+  const int row = q.q0 + j;
+  const int pos = q.c0 + j;
+  const int lb = pos >> __builtin_ctz(BS);           // floor division
+  const bool ok = (j < q.nl) & (row >= 0) & (row < a.n_tokens) & (pos >= 0) & (lb < a.bt_stride) &
+                  (b >= 0) & (b < a.num_blocks);
+  *row_out = ok ? row : 0;
+  return ok ? (long)b * BS + (pos & (BS - 1)) : -1;
+}
+
+// Block-table entry lb of sequence s, clamped into the row so that the load is always in
+// bounds (a clamped entry is never used: dest_slot rejects lb outside [0, bt_stride)).
+__device__ __forceinline__ int bt_entry(const AppendArgs& a, int s, int lb) {
+  return a.bt[(size_t)s * a.bt_stride + min(max(lb, 0), a.bt_stride - 1)];
+}
+
+// bf16 GQA pool [NB][Hkv][16][d]: a workgroup appends kGqaTokensPerBlock tokens of one
+// sequence; thread r copies 16-byte chunk r of each token's K|V (2 * Hkv * d / 8 chunks).
+// The destinations are resolved once, before any store, so the metadata loads are scalar;
+// then every thread issues its loads for all the tokens before its first store (the
+// compiler may not move a load past a store to the pool, which could alias the input).
 __global__ __launch_bounds__(256) void append_gqa_kernel(AppendArgs a) {
   const int s = blockIdx.y;
   const int chunks = a.head_dim / 8;                 // 16-byte chunks per head row
   const int per_tok = a.num_kv_heads * chunks;       // chunks of one token's K (or V)
   const int j0 = blockIdx.x * kGqaTokensPerBlock;
-  for (int idx = threadIdx.x; idx < kGqaTokensPerBlock * 2 * per_tok; idx += blockDim.x) {
-    const int t = idx / (2 * per_tok);
-    const int r = idx - t * 2 * per_tok;
+  static_assert(kGqaTokensPerBlock <= 16, "a workgroup's tokens span at most two 16-token blocks");
+  const SeqAppend sq = seq_append(a, s);
+  const int lb0 = (sq.c0 + j0) >> 4;
+  const int b0 = bt_entry(a, s, lb0), b1 = bt_entry(a, s, lb0 + 1);
+  long slot[kGqaTokensPerBlock];
+  int row[kGqaTokensPerBlock];
+#pragma unroll
+  for (int t = 0; t < kGqaTokensPerBlock; ++t)
+    slot[t] = dest_slot<16>(a, sq, j0 + t, ((sq.c0 + j0 + t) >> 4) == lb0 ? b0 : b1, &row[t]);
+  for (int r = threadIdx.x; r < 2 * per_tok; r += blockDim.x) {
     const int kv = r >= per_tok;
     const int hc = r - kv * per_tok;                 // head * chunks + chunk
-    int row;
-    const long slot = dest_slot(a, s, j0 + t, &row);
-    if (slot < 0) continue;
     const int h = hc / chunks, c = hc - h * chunks;
-    const long blk = slot / a.block_size, rr = slot - blk * a.block_size;
-    const uint16_t* src = (kv ? a.v_new : a.k_new) + ((size_t)row * a.num_kv_heads * a.head_dim) + 8 * hc;
-    uint16_t* dst = (kv ? a.v_out : a.k_out) +
-                    (((size_t)blk * a.num_kv_heads + h) * a.block_size + rr) * a.head_dim + 8 * c;
-    st16(dst, ld16(src));
+    const uint16_t* src = (kv ? a.v_new : a.k_new) + 8 * hc;
+    uint16_t* dst = (kv ? a.v_out : a.k_out) + (size_t)h * 16 * a.head_dim + 8 * c;
+    u32x4 v[kGqaTokensPerBlock];
+#pragma unroll
+    for (int t = 0; t < kGqaTokensPerBlock; ++t) v[t] = ld16(src + (size_t)row[t] * per_tok * 8);
+#pragma unroll
+    for (int t = 0; t < kGqaTokensPerBlock; ++t) {
+      if (slot[t] < 0) continue;
+      const long blk = slot[t] >> 4, rr = slot[t] & 15;
+      st16(dst + ((size_t)blk * a.num_kv_heads * 16 + rr) * a.head_dim, v[t]);
+    }
   }
 }
 
-// FP8 pool [NB][bs][D] + scales [NB][bs]: one wave per token.  Lane l holds the 8-element
+// FP8 pool [NB][64][D] + scales [NB][64]: one wave per token.  Lane l holds the 8-element
 // chunks l, l + 64, ... of the row in registers (D <= 1024), so the row is read once.
 template <int D>
 __global__ __launch_bounds__(64 * kFp8WavesPerBlock) void append_fp8_kernel(AppendArgs a) {
@@ -72,8 +102,9 @@ __global__ __launch_bounds__(64 * kFp8WavesPerBlock) void append_fp8_kernel(Appe
   const int s = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.x * kFp8WavesPerBlock + (threadIdx.x >> 6);
+  const SeqAppend sq = seq_append(a, s);
   int row;
-  const long slot = dest_slot(a, s, j, &row);
+  const long slot = dest_slot<64>(a, sq, j, bt_entry(a, s, (sq.c0 + j) >> 6), &row);
   if (slot < 0) return;                              // the whole wave agrees
   const uint16_t* src = a.k_new + (size_t)row * D;
   float x[kPer][8];
