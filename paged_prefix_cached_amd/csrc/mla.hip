@@ -125,6 +125,11 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
   __shared__ __attribute__((aligned(16))) f32x4 xs[SPLIT > 1 ? NW * 4 * 64 : 1];  // partial S
   __shared__ int32_t bt_s[SPARSE ? (STAGED ? kBtLds : 1) : kDecodeSplitMla / kBs + 1];
   __shared__ int32_t sel_s[SPARSE && STAGED ? kSelLds : 1];
+  // Decode (two waves a SIMD) keeps its first Q fragment in LDS, one 16-byte read per tile,
+  // instead of a register: the register file is the limit there, and a spilled fragment
+  // would be reloaded from scratch memory inside the pipeline.
+  constexpr int kQL = SPARSE ? 0 : 1;
+  __shared__ __attribute__((aligned(16))) u32x4 qls[kQL > 0 ? kQL * NT : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keep it scalar
@@ -191,7 +196,11 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
 #pragma unroll
     for (int ks = 0; ks < kQW; ++ks) {
       const u32x4 v = ld16(qp + 16 * ks);
-      qb[ks] = u32x4{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
+      const u32x4 f = u32x4{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
+      if (ks < kQL)
+        qls[ks * NT + tid] = f;
+      else
+        qb[ks] = f;
     }
   }
 
@@ -335,22 +344,41 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
     convert_meta(P);
   };
 
-  // ---- per-lane LDS offsets (fp16 units) into an fp16 tile, swizzle folded in.
+  // ---- per-lane LDS offsets (fp16 units) into an fp16 tile, swizzle folded in.  They are
+  // recomputed from an opaque copy of the lane id where each phase starts, so that none
+  // of them holds a register through the other phases (the register file is the limit).
+  auto fresh_lane = []() -> int {
+    int ln = (int)__lane_id();
+    asm volatile("" : "+v"(ln));
+    return ln;
+  };
   // K fragment of k-step ks (0..35): key row l32, logical chunk 2ks + h stored at chunk
-  // (2ks + h) ^ v, v = (l32 / 4) & 3; ks parity decides the sign of the v/2 term.
-  const int vk = (l32 >> 2) & 3;
-  int k_even = l32 * kKS + 8 * (h ^ (vk & 1)) + 16 * (vk >> 1);
-  int k_odd = l32 * kKS + 8 * (h ^ (vk & 1)) - 16 * (vk >> 1);
-  if ((kQW * half) & 1) {   // this wave's first k-step is odd: swap the two bases
-    const int t = k_even; k_even = k_odd; k_odd = t;
-  }
+  // (2ks + h) ^ v, v = (l32 / 4) & 3; ks parity decides the sign of the v/2 term.  The
+  // pair (even-step base, odd-step base) is swapped when this wave's first step is odd.
+  auto k_bases = [&](int& k_even, int& k_odd) {
+    const int ln = fresh_lane();
+    const int r = ln & 31, hh = ln >> 5, vk = (r >> 2) & 3;
+    const int base = r * kKS + 8 * (hh ^ (vk & 1));
+    k_even = base + 16 * (vk >> 1);
+    k_odd = base - 16 * (vk >> 1);
+    if ((kQW * half) & 1) {
+      const int t = k_even; k_even = k_odd; k_odd = t;
+    }
+  };
   // V^T fragments of k-step kk and output tile mt: rows 16kk + 4h + n/4 (first read) and
   // 8 rows further (second), logical chunk 4mt + 2(g%2) + (n%4)/2, fp16 offset 4(n&1).
-  const int g = lane >> 4, n = lane & 15;
-  const int vrow = 4 * h + (n >> 2);
-  const int vsub = 2 * (g & 1) + ((n & 3) >> 1);
-  const int v_lo = vrow * kKS + 8 * (vsub ^ h) + 4 * (n & 1);
-  const int v_hi = (vrow + 8) * kKS + 8 * (vsub ^ ((h + 2) & 3)) + 4 * (n & 1);
+  auto v_bases = [&](int& v_lo, int& v_hi) {
+    const int ln = fresh_lane();
+    const int hh = ln >> 5, gg = ln >> 4, n = ln & 15;
+    const int vrow = 4 * hh + (n >> 2);
+    const int vsub = 2 * (gg & 1) + ((n & 3) >> 1);
+    v_lo = vrow * kKS + 8 * (vsub ^ hh) + 4 * (n & 1);
+    v_hi = (vrow + 8) * kKS + 8 * (vsub ^ ((hh + 2) & 3)) + 4 * (n & 1);
+  };
+  // this wave's S share slot, and the first share of its pair
+  auto x_own = [&]() -> f32x4* { return xs + (SPLIT > 1 ? wave * 256 + fresh_lane() : 0); };
+  auto x_pair = [&]() -> const f32x4* { return xs + (SPLIT > 1 ? (wave - half) * 256 + fresh_lane() : 0); };
+  auto x_partner = [&]() -> const f32x4* { return xs + (SPLIT == 2 ? (wave ^ 1) * 256 + fresh_lane() : 0); };
 
   f32x16 acc[kMW];
 #pragma unroll
@@ -358,18 +386,28 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  f32x4* x_own = xs + (SPLIT > 1 ? wave * 256 + lane : 0);
-  const f32x4* x_pair = xs + (SPLIT > 1 ? (wave - half) * 256 + lane : 0);   // share 0's partial
 
-  // Other half of the wave (lane ^ 32) without an LDS round trip.
-  auto other_half = [](float v) -> float {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
+  // Max / sum of a value over lanes l and l ^ 32, without an LDS round trip and without
+  // the lane id: after the swap one copy holds the low half's values in both halves and
+  // the other the high half's, so every lane combines the same two operands in the same
+  // order.
+  auto halves = [](float v) {
+    return __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  };
+  auto halves_max = [&](float v) -> float {
+    const auto r = halves(v);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  };
+  auto halves_sum = [&](float v) -> float {
+    const auto r = halves(v);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
   };
 
   // ---- stage 3a: S^T[32 keys x 32 rows] over this wave's share of the 576 dims
   auto qk = [&](auto P) -> f32x16 {
     const uint16_t* F = fb[P];
+    int k_even, k_odd;
+    k_bases(k_even, k_odd);
     f32x16 s;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
@@ -377,21 +415,35 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
     for (int k = 0; k < kQW; ++k) {
       const int ks = kQW * half + k;             // bases swapped above when kQW * half is odd
       const uint16_t* kp = F + ((k & 1) ? k_odd : k_even) + 16 * ks;
-      s = mfma32x32x16_f16(*reinterpret_cast<const u32x4*>(kp), qb[k], s);
+      s = mfma32x32x16_f16(*reinterpret_cast<const u32x4*>(kp), k < kQL ? qls[k * NT + tid] : qb[k], s);
     }
     return s;
   };
   // ---- stage 3b: full S, online softmax, O^T += V^T P^T for this wave's output dims
-  auto softmax_pv = [&](auto P, f32x16 s, int t, bool conv_next) {
+  auto softmax_pv = [&](auto P, f32x16 s_in, int t, bool conv_next) {
     const uint16_t* F = fb[P];
-    if constexpr (SPLIT > 1) {
-      // rebuild the full S from all published shares in one fixed order -- the same
-      // operations in every wave of the group
+    // scalars, not a 16-register tuple: per-element updates then need no tuple copies
+    float s[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = s_in[i];
+    if constexpr (SPLIT == 2) {
+      // the full S = own share + partner's share; float addition is commutative, so both
+      // waves of the pair get bit-identical sums
+      const f32x4* xq = x_partner();
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 a = x_pair[64 * i4], b = x_pair[256 + 64 * i4];
-        f32x4 sum = a + b;
-        if constexpr (SPLIT == 4) sum = sum + (x_pair[512 + 64 * i4] + x_pair[768 + 64 * i4]);
+        const f32x4 b = xq[64 * i4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[4 * i4 + i] += b[i];
+      }
+    } else if constexpr (SPLIT == 4) {
+      // rebuild the full S from all published shares in one fixed order -- the same
+      // operations in every wave of the group
+      const f32x4* xp = x_pair();
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 a = xp[64 * i4], b = xp[256 + 64 * i4];
+        const f32x4 sum = (a + b) + (xp[512 + 64 * i4] + xp[768 + 64 * i4]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[4 * i4 + i] = sum[i];
       }
@@ -422,7 +474,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
         }
       }
     }
-    mx = fmaxf(mx, other_half(mx));
+    mx = halves_max(mx);
     // The reference maximum moves only when a row's maximum grows by more than 2^8
     // (log2 units): probabilities stay <= 256, exact enough in fp16, and the accumulator
     // is rescaled almost never.  Softmax does not depend on the reference.
@@ -457,6 +509,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
     // the next tile's upcast (independent of this P.V) in the same block as the MFMAs
     constexpr int Q = 1 - decltype(P)::value;
     if (conv_next) convert_chunks(Int<Q>{});
+    int v_lo, v_hi;
+    v_bases(v_lo, v_hi);
 #pragma unroll
     for (int mt = 0; mt < kMW; ++mt) {
       const int col = 32 * (kMW * half + mt);
@@ -483,7 +537,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
   auto publish = [&](const f32x16& s) {
     if constexpr (SPLIT > 1) {
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) x_own[64 * i4] = f32x4{s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3]};
+      for (int i4 = 0; i4 < 4; ++i4) {
+        f32x4* xo = x_own();
+        xo[64 * i4] = f32x4{s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3]};
+      }
     }
   };
   auto step = [&](auto P, int t) {
@@ -520,7 +577,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
   }
 
   // ---- finish: full row sum over the two lane halves, write this wave's dims
-  const float l_tot = l_run + other_half(l_run);
+  const float l_tot = halves_sum(l_run);
   if (!row_ok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse2 = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;

@@ -66,13 +66,22 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t u) {
                                                                   __uint_as_float(u & 0xffff0000u)));
 }
 
-// Four OCP E4M3FN bytes -> four fp16, exact (every E4M3 value is an fp16 normal).
+// Four OCP E4M3FN bytes -> four fp16, exact (every E4M3 value is an fp16 normal).  The
+// gfx950 scaled converter with scale 1 writes two fp16 per instruction.
+#ifndef PA_CVT_SCALED
+#define PA_CVT_SCALED 1
+#endif
 __device__ __forceinline__ u32x2 fp8x4_to_f16x4(uint32_t src) {
+  u32x2 r;
+#if PA_CVT_SCALED
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)src, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)src, 1.0f, true));
+#else
   const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)src, false);
   const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)src, true);
-  u32x2 r;
   r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo.x, lo.y));
   r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi.x, hi.y));
+#endif
   return r;
 }
 
@@ -82,14 +91,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Four OCP E4M3FN bytes -> four bf16 (exact: every E4M3 value is a bf16 value).  The
-// hardware converter gives fp32; the bf16 is its upper half.
+// Four OCP E4M3FN bytes -> four bf16 (exact: every E4M3 value is a bf16 value), two per
+// instruction with the gfx950 scaled converter (scale 1); otherwise the fp32 converter
+// and the upper halves.
 __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t src) {
+  u32x2 r;
+#if PA_CVT_SCALED
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)src, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)src, 1.0f, true));
+#else
   f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)src, false);
   f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)src, true);
-  u32x2 r;
   r.x = __builtin_amdgcn_perm(__float_as_uint(lo.y), __float_as_uint(lo.x), 0x07060302u);
   r.y = __builtin_amdgcn_perm(__float_as_uint(hi.y), __float_as_uint(hi.x), 0x07060302u);
+#endif
   return r;
 }
 
