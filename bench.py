@@ -209,6 +209,93 @@ def bench_prefill(steps, warmup):
                          "unit": "TFLOP/s", "frac": flops / (k_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}}
 
 
+def _bench_gqa_prefill_workload(wl, label, steps, warmup):
+    """Time paged_attn_prefill on a generated GQA workload; MFMA roofline on the causal
+    (query, visible key) pairs: 4 d FLOP each per query head."""
+    import torch
+    import paged_prefix_cached_amd as pa
+    from workloads.device import GqaOnDevice
+    dev = GqaOnDevice(wl)
+    del wl.k_pool, wl.v_pool
+    out = torch.empty((wl.q.shape[0], wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        pa.paged_attn_prefill(dev.q, dev.pool, dev.bt, dev.cached, dev.n_new, dev.q_start,
+                              num_q_heads=wl.num_q_heads, max_new_len=dev.max_new,
+                              max_total_len=dev.max_total, scale=wl.scale, out=out)
+
+    ms, kern = timed_steps(step, steps, warmup)
+    pairs = sum(int(c) * int(n) + int(n) * (int(n) + 1) // 2
+                for c, n in zip(wl.total_len - wl.n_new, wl.n_new))
+    flops = pairs * wl.num_q_heads * 4 * wl.head_dim
+    k_ms = kern.get("prefill_gqa", float("nan"))
+    return {"workload": label, "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "tokens_per_s": wl.q.shape[0] / (ms * 1e-3), "kernel_ms": kern, "flop": flops,
+            "roofline": {"bound": "mfma", "achieved": flops / (k_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": flops / (k_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}}
+
+
+def bench_cold(steps, warmup):
+    import workloads as W
+    t = time.time()
+    wl = W.make_cold_prefill(7)
+    log(f"[bench] cold-prompt workload ready in {time.time() - t:.1f}s")
+    return _bench_gqa_prefill_workload(
+        wl, "cold-prompt prefill: 4 seqs x 32768 new tokens (nothing cached), 32q/8kv, d128, bf16", steps, warmup)
+
+
+def bench_chunked(steps, warmup):
+    """One step of the chunked-prefill scheduler, the way an engine issues it: one
+    paged_attn_prefill call for the requests that advance by a prefill chunk and one
+    paged_attn_decode call for the requests that add a single token."""
+    import torch
+    import paged_prefix_cached_amd as pa
+    import workloads as W
+    from workloads.device import t as to_dev
+    t = time.time()
+    wl = W.make_chunked_mixed(8)
+    log(f"[bench] chunked-step workload ready in {time.time() - t:.1f}s")
+    nc = int((wl.n_new > 1).sum())                       # chunked requests come first
+    S = wl.num_seqs
+    kd, vd = to_dev(wl.k_pool, "cuda"), to_dev(wl.v_pool, "cuda")
+    del wl.k_pool, wl.v_pool
+    pool = pa.gqa_pool(kd, vd)
+    bt = to_dev(wl.block_table, "cuda")
+    q = to_dev(wl.q, "cuda")
+    cached = (wl.total_len - wl.n_new).astype(np.int32)
+    p_bt, p_cached = bt[:nc], to_dev(cached[:nc], "cuda")
+    p_new, p_qs = to_dev(wl.n_new[:nc].astype(np.int32), "cuda"), to_dev(wl.q_start[:nc + 1].astype(np.int32), "cuda")
+    n_pq = int(wl.q_start[nc])
+    d_bt, d_ctx = bt[nc:], to_dev(wl.total_len[nc:].astype(np.int32), "cuda")
+    d_q = q[n_pq:].view(S - nc, 1, wl.num_q_heads, wl.head_dim)
+    max_new, max_total = int(wl.n_new[:nc].max()), int(wl.total_len[:nc].max())
+    max_ctx = int(wl.total_len[nc:].max())
+    out_p = torch.empty((n_pq, wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    out_d = torch.empty((S - nc, 1, wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    nws = pa.load().paged_attn_decode_workspace_size(S - nc, 1, wl.num_q_heads, max_ctx, pa.ctypes.byref(pool))
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+
+    def step():
+        pa.paged_attn_prefill(q[:n_pq], pool, p_bt, p_cached, p_new, p_qs, num_q_heads=wl.num_q_heads,
+                              max_new_len=max_new, max_total_len=max_total, scale=wl.scale, out=out_p)
+        pa.paged_attn_decode(d_q, pool, d_bt, d_ctx, q_per_seq=1, num_q_heads=wl.num_q_heads,
+                             max_context_len=max_ctx, scale=wl.scale, out=out_d, workspace=ws)
+
+    ms, kern = timed_steps(step, steps, warmup)
+    pairs = sum(int(c) * int(n) + int(n) * (int(n) + 1) // 2 for c, n in zip(cached[:nc], wl.n_new[:nc]))
+    flops = pairs * wl.num_q_heads * 4 * wl.head_dim
+    kv_bytes = int(wl.total_len[nc:].astype(np.int64).sum()) * wl.num_kv_heads * wl.head_dim * 4
+    k_ms = kern.get("prefill_gqa", float("nan"))
+    return {"workload": "chunked-prefill step: 4 x 512-token chunks (prefill call) + 60 decode tokens "
+                        "(decode call), contexts log-uniform 4K-142K, 32q/8kv, d128, bf16",
+            "ms": ms, "tokens_per_s": wl.q.shape[0] / (ms * 1e-3), "kernel_ms": kern, "flop": flops,
+            "decode_kv_bytes": kv_bytes,
+            "decode_kv_gbps": kv_bytes / (kern.get("decode_gqa", float("nan")) * 1e-3) / 1e9,
+            "roofline": {"bound": "mfma", "achieved": flops / (k_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": flops / (k_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                         "kernel": "gqa_prefill_kernel"}}
+
+
 def bench_mla(steps, warmup):
     import torch
     import paged_prefix_cached_amd as pa
@@ -346,7 +433,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--secondary", default="", help="comma list of extra workloads: 2n (decode with no "
                                                     "shared blocks), 3 (prefill), 4 (MLA MTP3 decode), "
-                                                    "5 (indexer + sparse MLA), a (KV append)")
+                                                    "5 (indexer + sparse MLA), a (KV append), c (cold-prompt prefill), "
+                                                    "m (chunked-prefill step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (reference kernel for HBM counters)")
@@ -385,7 +473,8 @@ def main():
                                                               "tokens_per_s", "kernel_ms", "roofline")}
                 continue
             f = {"3": ("prefill_suffix", bench_prefill), "4": ("mla_decode_mtp3", bench_mla),
-                 "5": ("indexer_topk_sparse_mla", bench_sparse), "a": ("kv_append", bench_append)}[c]
+                 "5": ("indexer_topk_sparse_mla", bench_sparse), "a": ("kv_append", bench_append),
+                 "c": ("cold_prompt_prefill", bench_cold), "m": ("chunked_prefill_step", bench_chunked)}[c]
             sec[f[0]] = f[1](max(2, args.steps // 4), max(1, args.warmup // 2))
             torch.cuda.empty_cache()
         line["secondary"] = sec

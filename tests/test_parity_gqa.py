@@ -138,3 +138,56 @@ def test_decode_full_size_sampled(pa_lib):
         ro, rl = oracle.paged_gqa_attention(wl, s)
         assert_close(got[s:s + 1], ro, BF16_MAX_ABS, BF16_L1, f"decode full seq={s} L={wl.total_len[s]}")
         np.testing.assert_allclose(lg[s:s + 1], rl, atol=LSE_ABS)
+
+
+# --------------------------------------------------------------------------- cold prompts and
+# chunked-prefill steps (a workgroup takes a tile and its mirror in the sequence)
+@pytest.mark.parametrize("G,D,new", [(4, 128, 1000), (8, 64, 1000), (1, 128, 300), (2, 64, 129)])
+def test_prefill_cold_prompt(pa_lib, G, D, new):
+    """Nothing cached: causal over the prompt itself.  Tile counts even and odd (a middle
+    tile without a mirror), and a last partial tile."""
+    wl = W.make_cold_prefill(60 + G, num_seqs=2, new=new, num_q_heads=2 * G, num_kv_heads=2,
+                             head_dim=D, keep_content=True)
+    dev = GqaOnDevice(wl)
+    out, lse = _prefill(pa_lib, dev)
+    got, lg = bf16_out(out), lse.cpu().numpy()
+    for s in range(wl.num_seqs):
+        ro, rl = oracle.paged_gqa_attention(wl, s)
+        a, b = wl.q_start[s], wl.q_start[s + 1]
+        assert_close(got[a:b], ro, BF16_MAX_ABS, BF16_L1, f"cold prompt G={G} D={D} seq={s}")
+        np.testing.assert_allclose(lg[a:b], rl, atol=LSE_ABS)
+
+
+def test_prefill_chunked_step(pa_lib):
+    """A chunked-prefill step: two requests advance by a prefill chunk on top of their
+    context, five add one decode token, in one call."""
+    wl = W.make_chunked_mixed(8, n_chunked=2, chunk=130, n_decode=5, lo=200, hi=2000,
+                              num_q_heads=8, num_kv_heads=2, head_dim=128, keep_content=True)
+    dev = GqaOnDevice(wl)
+    out, lse = _prefill(pa_lib, dev)
+    got, lg = bf16_out(out), lse.cpu().numpy()
+    for s in range(wl.num_seqs):
+        ro, rl = oracle.paged_gqa_attention(wl, s)
+        a, b = wl.q_start[s], wl.q_start[s + 1]
+        assert_close(got[a:b], ro, BF16_MAX_ABS, BF16_L1, f"chunked step seq={s}")
+        np.testing.assert_allclose(lg[a:b], rl, atol=LSE_ABS)
+
+
+def test_prefill_cold_prompt_full_size_sampled(pa_lib):
+    """The benchmarked cold-prompt shape (32,768 new tokens, 32q/8kv, d128; one sequence
+    of the batch), checked on sampled query rows with the oracle's attention over the
+    rows' visible keys."""
+    wl = W.make_cold_prefill(7, num_seqs=1, new=32768, keep_content=False)
+    dev = GqaOnDevice(wl)
+    out, lse = _prefill(pa_lib, dev)
+    got, lg = bf16_out(out), lse.cpu().numpy()
+    L = int(wl.total_len[0])
+    kp = np.swapaxes(wl.k_pool, 1, 2)
+    vp = np.swapaxes(wl.v_pool, 1, 2)
+    k = oracle.bf16_to_f64(oracle.gather_paged(kp, wl.block_table[0], L))
+    v = oracle.bf16_to_f64(oracle.gather_paged(vp, wl.block_table[0], L))
+    rows = np.array([0, 1, 31, 32, 4095, 16383, 16384, 32736, 32767])
+    q = oracle.bf16_to_f64(wl.q[rows])
+    ro, rl = oracle.attention(q, k, v, rows, wl.scale)
+    assert_close(got[rows], ro, BF16_MAX_ABS, BF16_L1, "cold prompt 32768 sampled rows")
+    np.testing.assert_allclose(lg[rows], rl, atol=LSE_ABS)

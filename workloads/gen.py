@@ -32,6 +32,7 @@ __all__ = [
     "fp8_quantize_tokens", "normal_f32", "PagedGQA", "PagedMLA", "IndexerInput",
     "make_prefill_tiny", "make_gqa_decode", "make_prefix_prefill", "make_mla_decode",
     "make_sparse_mla", "make_gqa", "tie_scores", "CONFIG_NAMES", "AppendInput", "make_append",
+    "make_cold_prefill", "make_chunked_mixed",
 ]
 
 BF16_NAN = np.uint16(0x7FC0)
@@ -331,6 +332,36 @@ def make_prefix_prefill(seed: int = 3, *, num_seqs: int = 8, cached: int = 14200
     return make_gqa(seed, lengths=lengths, n_new=np.full(num_seqs, new), num_q_heads=num_q_heads,
                     num_kv_heads=num_kv_heads, head_dim=head_dim, q_mult=q_mult,
                     keep_content=keep_content, name=CONFIG_NAMES[3])
+
+
+def make_cold_prefill(seed: int = 7, *, num_seqs: int = 4, new: int = 32768, num_q_heads: int = 32,
+                      num_kv_heads: int = 8, head_dim: int = 128, keep_content: bool = False) -> PagedGQA:
+    """Cold prompts: nothing cached, the whole prompt is new and causal over itself.  The
+    vLLM AgentX article (news.ainew.jp), "Two-level scheduling", names the rare long fresh
+    prefills that fill the prefix cache; the GLM-5.3 report (aisoku.org), "What's new",
+    measures PCP on 32K prompts."""
+    lengths = np.full(num_seqs, new)
+    return make_gqa(seed, lengths=lengths, n_new=lengths, num_q_heads=num_q_heads,
+                    num_kv_heads=num_kv_heads, head_dim=head_dim, keep_content=keep_content,
+                    name=f"cold prompt prefill ({num_seqs} x {new} new, no cached prefix)")
+
+
+def make_chunked_mixed(seed: int = 8, *, n_chunked: int = 4, chunk: int = 512, n_decode: int = 60,
+                       lo: float = 4000, hi: float = 142000, num_q_heads: int = 32,
+                       num_kv_heads: int = 8, head_dim: int = 128,
+                       keep_content: bool = False) -> PagedGQA:
+    """One step of the chunked-prefill scheduler: the vLLM AgentX article, "Two-level
+    scheduling" (resolving head-of-line blocking), caps one request's tokens per step at 512
+    so that short turns share the step.  n_chunked requests advance by a chunk-token prefill
+    chunk on top of what they hold; n_decode requests add one token.  Contexts are
+    log-uniform in [lo, hi]."""
+    rng = _rng(seed, 30)
+    ctx = np.floor(np.exp(rng.uniform(math.log(lo), math.log(hi), n_chunked + n_decode))).astype(np.int64)
+    lengths = np.concatenate([ctx[:n_chunked] + chunk, ctx[n_chunked:]])
+    n_new = np.concatenate([np.full(n_chunked, chunk), np.ones(n_decode, np.int64)])
+    return make_gqa(seed, lengths=lengths, n_new=n_new, num_q_heads=num_q_heads,
+                    num_kv_heads=num_kv_heads, head_dim=head_dim, keep_content=keep_content,
+                    name=f"chunked-prefill step ({n_chunked} x {chunk}-token chunks + {n_decode} decode tokens)")
 
 
 # --------------------------------------------------------------------------- MLA (FP8 latent)
