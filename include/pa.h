@@ -121,6 +121,12 @@ int32_t pa_version(void);
  *   lse       dev fp32 [total_q][num_q_heads] or NULL.
  * Supported: PA_BF16, block_size 16, head_dim 64 or 128, num_q_heads/num_kv_heads in
  * {1, 2, 4, 8}.
+ * Workspace: when the new-token tiles are too few to fill the GPU and the contexts are
+ * long (a chunked-prefill step: [AgentX] "Two-level scheduling", 512-token chunks), the
+ * keys of each tile are split into ranges whose partial (output, log-sum-exp) pairs are
+ * merged in a fixed order; paged_attn_prefill_workspace_size() then returns the bytes of
+ * those partials (0 when the call runs unsplit).  The choice depends only on the sizes
+ * and the device, so the size query and the call agree; results are deterministic.
  * ------------------------------------------------------------------------------- */
 size_t paged_attn_prefill_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                          int32_t max_new_len, int32_t max_total_len,

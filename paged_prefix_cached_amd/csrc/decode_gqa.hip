@@ -527,13 +527,25 @@ constexpr int kCombineBatch = 8;   // partials loaded per lane before they are u
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   __shared__ f32x4 num_s[256];
   __shared__ float m_s[256], den_s[256];
-  const int row = blockIdx.x % a.rows, s = blockIdx.x / a.rows;
+  int row = blockIdx.x % a.rows, s = blockIdx.x / a.rows;
   const int D = a.head_dim, DV4 = D / 4, JL = 256 / DV4;
   const int tid = threadIdx.x, jl = tid / DV4, d4 = tid % DV4;
   size_t base;
   long stride;
   int n;
-  if (a.unit_start != nullptr) {
+  if (a.pf_q_start != nullptr) {
+    // split-K prefill: block (sequence, new token j, head); s becomes the packed token row
+    const int seq = s / a.pf_max_new, j = s % a.pf_max_new;
+    const int nl = min(a.pf_new_len[seq], a.pf_max_new);
+    if (j >= nl) return;                           // no such token: nothing to write
+    const int cached = a.pf_cached[seq];
+    const int total = min(cached + nl, a.pf_max_total);
+    const int vis = min(cached + j, total - 1) + 1;  // keys the token sees
+    n = vis > 0 ? min((vis + a.split - 1) / a.split, a.max_splits) : 0;
+    s = a.pf_q_start[seq] + j;
+    base = (size_t)s * a.max_splits * a.rows + row;
+    stride = a.rows;
+  } else if (a.unit_start != nullptr) {
     const int Hq = a.rows / a.q_per_seq, G = Hq / a.num_kv_heads, R = a.q_per_seq * G;
     const int t = row / Hq, hq = row % Hq, head = hq / G;
     const int g = s / a.members, m = s % a.members;
@@ -601,7 +613,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
-  const unsigned grid = (unsigned)a.num_seqs * a.rows;
+  const unsigned grid = (unsigned)a.num_seqs * (a.pf_q_start != nullptr ? (unsigned)a.pf_max_new : 1u) * a.rows;
   if (grid == 0) return hipSuccess;
   if (a.head_dim % 4 != 0 || a.head_dim / 4 > 256 || 256 % (a.head_dim / 4) != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(256), 0, stream, a);

@@ -153,8 +153,30 @@ const char* pa_last_error_detail(void) { return g_detail; }
 int32_t pa_version(void) { return 1; }
 
 // ------------------------------------------------------------------------- prefill
-size_t paged_attn_prefill_workspace_size(int32_t, int32_t, int32_t, int32_t, const pa_kv_pool*) {
-  return 0;
+// Split-K prefill workspace: partial o [num_seqs * max_new_len][max_splits][num_q_heads][d]
+// fp32, then the partial log2-sum-exp (each part 256-byte aligned).
+struct PrefillLayout {
+  int split_len, max_splits;
+  size_t o_bytes, lse_bytes;
+  size_t total() const { return o_bytes + lse_bytes; }
+};
+
+PrefillLayout prefill_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_new_len,
+                             int32_t max_total_len, const pa_kv_pool* pool) {
+  PrefillLayout l{};
+  if (pool == nullptr || pool->num_kv_heads < 1 || num_q_heads < 1 || num_seqs < 1 || max_new_len < 1) return l;
+  l.split_len = pa::prefill_split_len(num_seqs, num_q_heads, pool->num_kv_heads, max_new_len, max_total_len);
+  if (l.split_len == 0) return l;
+  l.max_splits = ceil_div(max_total_len, l.split_len);
+  const size_t rows = (size_t)num_seqs * max_new_len * l.max_splits * num_q_heads;
+  l.o_bytes = round_up(rows * pool->head_dim_v * sizeof(float), 256);
+  l.lse_bytes = round_up(rows * sizeof(float), 256);
+  return l;
+}
+
+size_t paged_attn_prefill_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t max_new_len,
+                                         int32_t max_total_len, const pa_kv_pool* pool) {
+  return prefill_layout(num_seqs, num_q_heads, max_new_len, max_total_len, pool).total();
 }
 
 pa_status paged_attn_prefill(const void* q, const pa_kv_pool* pool, const int32_t* block_table,
@@ -163,8 +185,6 @@ pa_status paged_attn_prefill(const void* q, const pa_kv_pool* pool, const int32_
                              int32_t max_new_len, int32_t max_total_len, float scale, void* out,
                              float* lse, void* workspace, size_t workspace_bytes,
                              hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   g_detail[0] = 0;
   PA_TRY(check_gqa_pool(pool));
   if (q == nullptr || out == nullptr || block_table == nullptr || cached_len == nullptr ||
@@ -182,6 +202,12 @@ pa_status paged_attn_prefill(const void* q, const pa_kv_pool* pool, const int32_
     return fail(PA_ERR_INVALID_ARG, "bt_stride * block_size < max_total_len");
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (num_seqs == 0 || max_new_len == 0) return PA_OK;
+  const PrefillLayout l = prefill_layout(num_seqs, num_q_heads, max_new_len, max_total_len, pool);
+  if (l.total() > 0) {
+    if (workspace == nullptr || workspace_bytes < l.total())
+      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", l.total(), workspace_bytes);
+    if (!aligned(workspace, 16)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
   pa::GqaPrefillArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(pool->k);
@@ -201,8 +227,32 @@ pa_status paged_attn_prefill(const void* q, const pa_kv_pool* pool, const int32_
   a.max_new_len = max_new_len;
   a.max_total_len = max_total_len;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.split_len = l.split_len;
+  a.max_splits = l.max_splits;
+  if (l.split_len > 0) {
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + l.o_bytes);
+  }
   (void)hipGetLastError();
-  return launched(timed("prefill_gqa", stream, [&] { return pa::launch_gqa_prefill(a, stream); }), "prefill launch");
+  PA_TRY(launched(timed("prefill_gqa", stream, [&] { return pa::launch_gqa_prefill(a, stream); }), "prefill launch"));
+  if (l.split_len == 0) return PA_OK;
+  pa::CombineArgs c{};
+  c.part_o = a.part_o;
+  c.part_lse = a.part_lse;
+  c.out = a.out;
+  c.lse = lse;
+  c.num_seqs = num_seqs;
+  c.rows = num_q_heads;
+  c.head_dim = pool->head_dim_v;
+  c.max_splits = l.max_splits;
+  c.split = l.split_len;
+  c.max_context_len = max_total_len;
+  c.pf_q_start = q_start;
+  c.pf_cached = cached_len;
+  c.pf_new_len = new_len;
+  c.pf_max_new = max_new_len;
+  c.pf_max_total = max_total_len;
+  return launched(timed("combine", stream, [&] { return pa::launch_combine(c, stream); }), "prefill combine launch");
 }
 
 // ------------------------------------------------------------------------- decode

@@ -49,7 +49,17 @@ struct GqaPrefillArgs {
   int32_t bt_stride, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks;
   int32_t max_new_len, max_total_len;
   float scale_log2;  // softmax scale * log2(e)
+  // Split-K (split_len > 0): the keys of a tile are cut into ranges of split_len; each
+  // workgroup writes the partial (o, log2-sum-exp) of one range for its rows at
+  // [token][split][num_q_heads] of part_o / part_lse, and the combine kernel merges them.
+  float* part_o;
+  float* part_lse;
+  int32_t split_len, max_splits;
 };
+// Key-range length for split-K prefill, or 0 when the prefill runs unsplit.  Depends only
+// on the sizes (and the device's compute-unit count), so that the workspace query and the
+// call agree.
+int prefill_split_len(int num_seqs, int num_q_heads, int num_kv_heads, int max_new_len, int max_total_len);
 
 struct GqaDecodeArgs {
   const uint16_t* q;
@@ -82,6 +92,12 @@ struct CombineArgs {
   // its group; otherwise partials are [S][max_splits][rows] with split `split`.
   const int32_t* unit_start;
   int32_t members, n_chunks, num_kv_heads, q_per_seq;
+  // Split-K prefill partials (pf_q_start != null): workgroup (s, j, head) merges the
+  // partials of new token j of sequence s, written at [token][split][rows] (rows = heads).
+  const int32_t* pf_q_start;
+  const int32_t* pf_cached;
+  const int32_t* pf_new_len;
+  int32_t pf_max_new, pf_max_total;
 };
 
 struct MlaDecodeArgs {

@@ -25,7 +25,7 @@
 // V (D + 32) fp16 (D/2 + 16 dwords, 16 or 48 mod 64: the 4 rows of a transpose read
 // phase hit distinct banks).
 // Workgroups of the same (sequence, KV head) are mapped onto one XCD so its L2 serves
-// the shared prefix to all of them.
+// the shared prefix to all of them; the XCDs take different KV heads.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -59,10 +59,15 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
   const int n_tiles = (a.max_new_len + TT - 1) / TT;
+  const int n_split = a.split_len > 0 ? a.max_splits : 1;
   const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
+  // tiles of one (sequence, key range) run together on one XCD (shared K/V in its L2);
+  // the KV head varies slowest, so the XCDs split the work by head and a long sequence
+  // is spread over all of them
   const int tile = logical % n_tiles;
-  const int g = (logical / n_tiles) % Hkv;
-  const int s = logical / (n_tiles * Hkv);
+  const int split = (logical / n_tiles) % n_split;
+  const int s = (logical / (n_tiles * n_split)) % a.num_seqs;
+  const int g = logical / (n_tiles * n_split * a.num_seqs);
   const int nl = min(a.new_len[s], a.max_new_len);
   const int tok0 = tile * TT;
   if (tok0 >= nl) return;
@@ -88,7 +93,11 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
   }
   // keys needed by this workgroup / this wave
   const int last_tok_wg = min(tok0 + TT, nl) - 1;
-  const int kv_end = min(cached + last_tok_wg + 1, total);
+  int kv_end = min(cached + last_tok_wg + 1, total);
+  // split-K: this workgroup's key range [kv_begin, kv_end)
+  const int kv_begin = a.split_len > 0 ? split * a.split_len : 0;
+  if (a.split_len > 0) kv_end = min(kv_end, kv_begin + a.split_len);
+  if (kv_begin >= kv_end) return;                      // no row of the tile sees this range
   const int wave_min_pos = cached + min(tok0 + (wave * kRowsPerWave) / G, nl - 1);
   const int wave_max_pos = min(cached + min(tok0 + (wave * kRowsPerWave + kRowsPerWave - 1) / G, nl - 1), total - 1);
   const float c = a.scale_log2;
@@ -212,15 +221,15 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
   };
 
   // ---- pipeline: one barrier per tile; buffer t&1 holds tile t
-  lookup_blocks(0);
-  load_kv(0);
+  lookup_blocks(kv_begin);
+  load_kv(kv_begin);
   store_tile(0);
-  if (kKT < kv_end) {
-    lookup_blocks(kKT);
-    load_kv(kKT);
+  if (kv_begin + kKT < kv_end) {
+    lookup_blocks(kv_begin + kKT);
+    load_kv(kv_begin + kKT);
   }
   __syncthreads();
-  for (int kt = 0, t = 0; kt < kv_end; kt += kKT, ++t) {
+  for (int kt = kv_begin, t = 0; kt < kv_end; kt += kKT, ++t) {
     const int buf = t & 1;
     if (kt + kKT < kv_end) {
       const bool more = kt + 2 * kKT < kv_end;
@@ -236,6 +245,19 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!row_ok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (a.split_len > 0) {
+    // partial of this key range: o (normalised over the range) and its log2-sum-exp
+    const size_t slot = ((size_t)(a.q_start[s] + tok_c) * a.max_splits + split) * Hq + g * G + hh;
+    float* po = a.part_o + slot * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(po + 32 * mt + 8 * q4 + 4 * h32) =
+            f32x4{acc[mt][4 * q4] * inv, acc[mt][4 * q4 + 1] * inv, acc[mt][4 * q4 + 2] * inv, acc[mt][4 * q4 + 3] * inv};
+    if (h32 == 0) a.part_lse[slot] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
+    return;
+  }
   uint16_t* op = a.out + q_row * D;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -264,11 +286,35 @@ hipError_t launch_d(const GqaPrefillArgs& a, int G, unsigned grid, hipStream_t s
 
 }  // namespace
 
+// Split-K when the unsplit grid would leave the compute units short of work and the key
+// ranges are long: 16,384-key ranges (a workgroup then handles at most 256 key tiles).
+#ifndef PA_PREFILL_SPLIT_LEN
+#define PA_PREFILL_SPLIT_LEN 16384
+#endif
+constexpr int kPrefillSplitLen = PA_PREFILL_SPLIT_LEN;
+int prefill_split_len(int num_seqs, int num_q_heads, int num_kv_heads, int max_new_len, int max_total_len) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || max_new_len <= 0) return 0;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  const int G = num_q_heads / num_kv_heads;
+  const int TT = kRows / (G > 0 ? G : 1);
+  const long wgs = (long)((max_new_len + TT - 1) / TT) * num_kv_heads * num_seqs;
+  if (wgs >= 4L * cus[dev] || max_total_len <= 2 * kPrefillSplitLen) return 0;
+  return kPrefillSplitLen;
+}
+
 hipError_t launch_gqa_prefill(const GqaPrefillArgs& a, hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int TT = kRows / G;
   const unsigned n_tiles = (unsigned)((a.max_new_len + TT - 1) / TT);
-  const unsigned grid = n_tiles * a.num_kv_heads * a.num_seqs;
+  const unsigned n_split = a.split_len > 0 ? (unsigned)a.max_splits : 1u;
+  const unsigned grid = n_tiles * n_split * a.num_kv_heads * a.num_seqs;
   if (grid == 0) return hipSuccess;
   return a.head_dim == 128 ? launch_d<128>(a, G, grid, stream) : launch_d<64>(a, G, grid, stream);
 }

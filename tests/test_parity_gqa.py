@@ -191,3 +191,24 @@ def test_prefill_cold_prompt_full_size_sampled(pa_lib):
     ro, rl = oracle.attention(q, k, v, rows, wl.scale)
     assert_close(got[rows], ro, BF16_MAX_ABS, BF16_L1, "cold prompt 32768 sampled rows")
     np.testing.assert_allclose(lg[rows], rl, atol=LSE_ABS)
+
+
+def test_prefill_split_k_long_contexts(pa_lib):
+    """Few, short new-token tiles over long contexts: the prefill splits each tile's keys
+    into 16,384-key ranges and merges the partials in a fixed order (decode tokens and
+    prefill chunks in one call)."""
+    wl = W.make_chunked_mixed(9, n_chunked=2, chunk=100, n_decode=3, lo=40000, hi=70000,
+                              num_q_heads=8, num_kv_heads=2, head_dim=128, keep_content=True)
+    dev = GqaOnDevice(wl)
+    assert pa_lib.load().paged_attn_prefill_workspace_size(
+        wl.num_seqs, 8, dev.max_new, dev.max_total, pa_lib.ctypes.byref(dev.pool)) > 0   # split-K taken
+    out, lse = _prefill(pa_lib, dev)
+    got, lg = bf16_out(out), lse.cpu().numpy()
+    for s in range(wl.num_seqs):
+        ro, rl = oracle.paged_gqa_attention(wl, s)
+        a, b = wl.q_start[s], wl.q_start[s + 1]
+        assert_close(got[a:b], ro, BF16_MAX_ABS, BF16_L1, f"split-K prefill seq={s}")
+        np.testing.assert_allclose(lg[a:b], rl, atol=LSE_ABS)
+    # fixed-order merge: bit-identical on a rerun
+    out2, lse2 = _prefill(pa_lib, dev)
+    assert bf16_out(out2).tobytes() == got.tobytes() and np.array_equal(lse2.cpu().numpy(), lg)
