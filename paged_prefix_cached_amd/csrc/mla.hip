@@ -166,10 +166,13 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
     const int rows = T * Hq;
     const int rblocks = (rows + RW - 1) / RW;
     const int n_units = da.num_seqs * da.max_splits * rblocks;
-    const int logical = xcd_swizzle(blockIdx.x, n_units);
+    // (sequence, split) units go to the XCDs round robin, with each sequence's split order
+    // rotated by its index: every XCD gets about 1/8 of every sequence's keys, whatever the
+    // mix of context lengths (the row blocks of a unit share its XCD's L2)
+    const int logical = xcd_unit_swizzle(blockIdx.x, n_units, rblocks);
     const int rb = logical % rblocks;
-    unit_split = (logical / rblocks) % da.max_splits;
     unit = logical / (rblocks * da.max_splits);
+    unit_split = ((logical / rblocks) % da.max_splits + unit) % da.max_splits;
     row0 = rb * RW;
     L = min(da.context_len[unit], da.max_context_len);
     k_begin = unit_split * kDecodeSplitMla;

@@ -144,6 +144,17 @@ __device__ __forceinline__ int32_t xcd_swizzle(int32_t hw_id, int32_t n) {
   return (hw_id & 7) * (n8 >> 3) + (hw_id >> 3);
 }
 
+// Work units of per_unit consecutive logical ids, dealt to the 8 XCDs round robin: XCD x
+// runs units x, x + 8, x + 16, ... (all ids of a unit on one XCD, sharing its L2), so the
+// XCDs get statistically equal work even when units differ in size along the id order.
+// Bijective on [0, n); ids past the last whole round of 8 units map to themselves.
+__device__ __forceinline__ int32_t xcd_unit_swizzle(int32_t hw_id, int32_t n, int32_t per_unit) {
+  const int32_t n8 = (n / (8 * per_unit)) * (8 * per_unit);
+  if (hw_id >= n8) return hw_id;
+  const int32_t k = hw_id >> 3;
+  return ((k / per_unit) * 8 + (hw_id & 7)) * per_unit + k % per_unit;
+}
+
 __device__ __forceinline__ float wave_max_xor(float v, int lanes) {
   for (int o = lanes >> 1; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
