@@ -10,7 +10,8 @@
 // The latent is shared by every query head, so attention is MQA with d_qk = 576 (512
 // latent + 64 rope) and d_v = 512 (the latent itself).  A workgroup holds NP wave pairs;
 // pair p owns 32 query rows and every pair reads the same keys (decode: 4 pairs = 128
-// rows, e.g. two MTP tokens x 64 heads; sparse: 2 pairs = the 64 heads of one query).
+// rows, e.g. two MTP tokens x 64 heads; sparse: two groups of four waves = the 64 heads of
+// one query, each wave a quarter of the dimensions).
 // Keys go in 32-key tiles through a three-stage pipeline:
 //   1. LDS-DMA (global_load_lds, 16 bytes a lane) gathers tile t+2's FP8 rows through the
 //      block table into a raw LDS buffer -- no registers held while the loads fly.  Block
@@ -39,6 +40,9 @@
 namespace pa {
 namespace {
 
+#ifndef PA_MLA_SPARSE_XCD
+#define PA_MLA_SPARSE_XCD 1
+#endif
 constexpr int kDqk = 576, kDv = 512, kBs = 64;
 constexpr int kKT = 32;                   // keys per tile
 constexpr int kKS = 608;                  // fp16 per LDS row: 1,216 B, 304 dwords = 48 mod 64
@@ -123,7 +127,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
   __shared__ __attribute__((aligned(16))) float fvs[2][kKT];     // scale
   __shared__ int32_t fall[2];                                    // 1: every key of the tile valid
   __shared__ __attribute__((aligned(16))) f32x4 xs[SPLIT > 1 ? NW * 4 * 64 : 1];  // partial S
-  __shared__ int32_t bt_s[SPARSE ? (STAGED ? kBtLds : 1) : kDecodeSplitMla / kBs + 1];
+  // eight-wave sparse workgroups stage only the selections (their LDS holds no block table)
+  constexpr bool STAGE_BT = STAGED && NW <= 4;
+  __shared__ int32_t bt_s[SPARSE ? (STAGE_BT ? kBtLds : 1) : kDecodeSplitMla / kBs + 1];
   __shared__ int32_t sel_s[SPARSE && STAGED ? kSelLds : 1];
   // Decode (two waves a SIMD) keeps its first Q fragment in LDS, one 16-byte read per tile,
   // instead of a register: the register file is the limit there, and a spilled fragment
@@ -149,8 +155,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
   if constexpr (SPARSE) {
     Hq = sa.num_q_heads;
     const int rblocks = (Hq + RW - 1) / RW;
-    const int i = blockIdx.x / rblocks;
-    row0 = (blockIdx.x % rblocks) * RW;
+    // consecutive query tokens select overlapping keys: keep them on one XCD (shared L2)
+    const int bid = PA_MLA_SPARSE_XCD ? xcd_swizzle(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+    const int i = bid / rblocks;
+    row0 = (bid % rblocks) * RW;
     unit = i;
     qbase = sa.q + (size_t)i * Hq * kDqk;
     kv = sa.kv; kv_scale = sa.kv_scale; num_blocks = sa.num_blocks;
@@ -158,7 +166,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
     sel_g = sa.topk + (size_t)i * sa.k;
     n_keys = sa.k;
     n_lblocks = sa.bt_stride;
-    n_bt = STAGED ? sa.bt_stride : 0;
+    n_bt = STAGE_BT ? sa.bt_stride : 0;
     scale_log2 = sa.scale_log2;
   } else {
     Hq = da.num_q_heads;
@@ -222,6 +230,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
         idx = sel_s[j];
         if (idx < 0) return -1;
         const int lb = idx / kBs;
+        if constexpr (!STAGE_BT) return phys_block(bt_row, lb, n_lblocks, num_blocks);
         return lb < n_bt ? bt_s[lb] : -1;
       } else {
         idx = sel_g[j];
@@ -619,12 +628,16 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
 #endif
 constexpr int kDecodeWaves = PA_MLA_DECODE_WAVES, kDecodeSplit = PA_MLA_DECODE_SPLIT;
 #ifndef PA_MLA_SPARSE_WAVES
-#define PA_MLA_SPARSE_WAVES 4
+#define PA_MLA_SPARSE_WAVES 8
 #endif
 #ifndef PA_MLA_SPARSE_SPLIT
-#define PA_MLA_SPARSE_SPLIT 2
+#define PA_MLA_SPARSE_SPLIT 4
 #endif
 constexpr int kSparseWaves = PA_MLA_SPARSE_WAVES, kSparseSplit = PA_MLA_SPARSE_SPLIT;
+#ifndef PA_MLA_SPARSE_STAGE
+#define PA_MLA_SPARSE_STAGE 1
+#endif
+constexpr bool kSparseStage = PA_MLA_SPARSE_STAGE != 0;   // selections and block ids staged in LDS
 constexpr int kDecodeRows = 32 * kDecodeWaves / kDecodeSplit, kSparseRows = 32 * kSparseWaves / kSparseSplit;
 
 }  // namespace
@@ -643,12 +656,15 @@ hipError_t launch_sparse_mla(const SparseMlaArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)a.n_q * ((a.num_q_heads + kSparseRows - 1) / kSparseRows);
   if (grid == 0) return hipSuccess;
   MlaDecodeArgs none{};
-  if (a.k <= kSelLds && a.bt_stride <= kBtLds)
-    hipLaunchKernelGGL((mla_kernel<true, kSparseWaves, kSparseSplit, true, true>), dim3(grid), dim3(64 * kSparseWaves), 0,
-                       stream, none, a);
-  else
-    hipLaunchKernelGGL((mla_kernel<true, kSparseWaves, kSparseSplit, false, true>), dim3(grid), dim3(64 * kSparseWaves), 0,
-                       stream, none, a);
+  if constexpr (kSparseStage) {
+    if (a.k <= kSelLds && (kSparseWaves > 4 || a.bt_stride <= kBtLds)) {
+      hipLaunchKernelGGL((mla_kernel<true, kSparseWaves, kSparseSplit, true, true>), dim3(grid), dim3(64 * kSparseWaves), 0,
+                         stream, none, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((mla_kernel<true, kSparseWaves, kSparseSplit, false, true>), dim3(grid), dim3(64 * kSparseWaves), 0,
+                     stream, none, a);
   return hipGetLastError();
 }
 
