@@ -119,17 +119,34 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
 #pragma unroll
     for (int j = 0; j < kKT / 16; ++j) pbs[j] = phys_block(bt_row, (kt >> 4) + j, n_lblocks, a.num_blocks);
   };
+  // Chunk i of a thread holds key tid / (D/8) + i * (256 / (D/8)) of the tile; the key's
+  // block is wave-uniform, so K and V are read through one buffer resource per (block, KV
+  // head): a scalar base plus a loop-invariant lane offset, no address arithmetic per load.
+  // A block past the sequence or out of range gets zero records (its loads return zeros);
+  // V rows past the sequence end (last tile only) are read at an offset past the records.
+  constexpr int kKeysPerRound = kThreads / (D / 8);     // keys covered by one round of chunks
   auto load_kv = [&](int kt) {
+    const bool tail = kt + kKT > total;                // uniform: the tile holds the end
+    __amdgpu_buffer_rsrc_t rk[kKT / 16], rv[kKT / 16];
+#pragma unroll
+    for (int j = 0; j < kKT / 16; ++j) {
+      const int pb = pbs[j];
+      const size_t blk = ((size_t)(pb >= 0 ? pb : 0) * Hkv + g) * head_stride;
+      rk[j] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + blk), (short)0, pb >= 0 ? 32 * D : 0, 0x00020000);
+      rv[j] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + blk), (short)0, pb >= 0 ? 32 * D : 0, 0x00020000);
+    }
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int ci = tid + kThreads * i;
-      const int key = ci / (D / 8), dc = ci % (D / 8);
-      int pb = pbs[0];
+      const int key = tid / (D / 8) + kKeysPerRound * i, dc = tid % (D / 8);
+      const int off = ((key & 15) * D + 8 * dc) * 2;      // bytes
+      const int j = __builtin_amdgcn_readfirstlane(key >> 4);
+      __amdgpu_buffer_rsrc_t ck = rk[0], cv = rv[0];
 #pragma unroll
-      for (int j = 1; j < kKT / 16; ++j) pb = (key >> 4) == j ? pbs[j] : pb;
-      const size_t off = ((size_t)pb * Hkv + g) * head_stride + (size_t)(key & 15) * D + 8 * dc;
-      kreg[i] = pb >= 0 ? ld16(a.k + off) : u32x4{0, 0, 0, 0};
-      vreg[i] = (pb >= 0 && kt + key < total) ? ld16(a.v + off) : u32x4{0, 0, 0, 0};
+      for (int q = 1; q < kKT / 16; ++q)
+        if (j == q) { ck = rk[q]; cv = rv[q]; }
+      kreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ck, off, 0, 0));
+      const int voff = (tail && kt + key >= total) ? (int)0x80000000 : off;
+      vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cv, voff, 0, 0));
     }
   };
   auto store_tile = [&](int buf) {
