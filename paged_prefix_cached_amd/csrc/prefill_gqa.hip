@@ -4,10 +4,12 @@
 // turn re-sends the history; most of it is a cached prefix, the new prefill is short)
 // and "Hybrid KV cache management" (one shared block pool, Figure 4).
 //
-// A workgroup owns 128 query rows of one (sequence, KV head): 128/G new tokens x the G
+// A workgroup owns 256 query rows of one (sequence, KV head): 256/G new tokens x the G
 // query heads that read that KV head, so every K/V tile staged in LDS serves all heads
-// of the group.  Four waves own 32 rows each.  The key loop walks the sequence's block
-// table in 64-key tiles (four 16-token blocks), one barrier per tile:
+// of the group.  Eight waves own 32 rows each (two per SIMD; the 148 KB of LDS for two
+// tile buffers leave one workgroup per CU): a tile fetched from HBM serves twice the
+// rows of a four-wave workgroup.  The key loop walks the sequence's block table in
+// 128-key tiles (eight 16-token blocks), one barrier per tile:
 //   * at the top of step t, tile t+1 (loaded into registers during step t-1, coalesced
 //     16-byte loads of contiguous (block, head) tiles) is stored into the other LDS
 //     buffer -- K row-major as bf16, V row-major as fp16 (exact conversion), V rows past
@@ -32,10 +34,18 @@
 namespace pa {
 namespace {
 
-constexpr int kThreads = 256;
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 8
+#endif
+constexpr int kWaves = PA_PREFILL_WAVES;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 32;
-constexpr int kRows = 4 * kRowsPerWave;   // 128 query rows per workgroup
-constexpr int kKT = 64;                   // keys per tile
+constexpr int kRows = kWaves * kRowsPerWave;   // query rows per workgroup
+#ifndef PA_PREFILL_KT
+#define PA_PREFILL_KT 128
+#endif
+constexpr int kKT = PA_PREFILL_KT;        // keys per tile
+constexpr int kST = kKT / 32;             // 32-key sub-tiles per tile
 
 template <int D>
 struct PrefillSmem {
@@ -109,7 +119,7 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
     for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;   // m_run in scaled log2 units
 
-  // ---- register prefetch of one K/V tile: chunk ci = tid + 256 i holds 8 dims of one key.
+  // ---- register prefetch of one K/V tile: chunk ci = tid + kThreads i holds 8 dims of one key.
   // A tile's four block ids are looked up first (same addresses in every lane); the K/V
   // loads go out together once they are back, so a tile costs one table round trip, not
   // one per chunk (vector-memory counters complete in order).
@@ -119,7 +129,7 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
 #pragma unroll
     for (int j = 0; j < kKT / 16; ++j) pbs[j] = phys_block(bt_row, (kt >> 4) + j, n_lblocks, a.num_blocks);
   };
-  // Chunk i of a thread holds key tid / (D/8) + i * (256 / (D/8)) of the tile; the key's
+  // Chunk i of a thread holds key tid / (D/8) + i * (kThreads / (D/8)) of the tile; the key's
   // block is wave-uniform, so K and V are read through one buffer resource per (block, KV
   // head): a scalar base plus a loop-invariant lane offset, no address arithmetic per load.
   // A block past the sequence or out of range gets zero records (its loads return zeros);
@@ -169,10 +179,10 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
   auto compute = [&](int buf, int kt) {
     const uint16_t* kt_s = sm.k[buf];
     const uint16_t* vt_s = sm.v[buf];
-    // ---- S^T = K Q^T, two 32-key sub-tiles
-    f32x16 sacc[2];
+    // ---- S^T = K Q^T, 32-key sub-tiles
+    f32x16 sacc[kST];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int st = 0; st < kST; ++st) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[st][i] = 0.f;
       const uint16_t* kp = kt_s + (32 * st + c32) * Sm::kStride + 8 * h32;
@@ -185,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
     if (kt + kKT - 1 > wave_min_pos) {
       // register i of sub-tile st holds key kt + 32 st + 4 h32 + 8 (i/4) + i%4
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < kST; ++st) {
         const int lim = pos - kt - 32 * st - 4 * h32;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -195,7 +205,7 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
       }
     } else {                                     // every key of the tile is visible
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < kST; ++st)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[st][i]);
     }
@@ -211,7 +221,7 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
     const float neg_m = m_run == -INFINITY ? 0.f : -m_run;   // fully masked rows: p = 0
     float rs = 0.f;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < kST; ++st)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = fast_exp2(fmaf(sacc[st][i], c, neg_m));
@@ -221,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
     l_run += rs;
     // ---- O^T += V^T P^T: k-step (st, kk) holds keys 32 st + 16 kk + 8 (j/4) + 4 h + j%4
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < kST; ++st)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int r0 = 8 * kk;
@@ -304,7 +314,7 @@ hipError_t launch_d(const GqaPrefillArgs& a, int G, unsigned grid, hipStream_t s
 }  // namespace
 
 // Split-K when the unsplit grid would leave the compute units short of work and the key
-// ranges are long: 16,384-key ranges (a workgroup then handles at most 256 key tiles).
+// ranges are long: 16,384-key ranges (a workgroup then handles at most 128 key tiles).
 #ifndef PA_PREFILL_SPLIT_LEN
 #define PA_PREFILL_SPLIT_LEN 16384
 #endif
