@@ -120,43 +120,48 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
   float m_run = -INFINITY, l_run = 0.f;   // m_run in scaled log2 units
 
   // ---- register prefetch of one K/V tile: chunk ci = tid + kThreads i holds 8 dims of one key.
-  // A tile's four block ids are looked up first (same addresses in every lane); the K/V
-  // loads go out together once they are back, so a tile costs one table round trip, not
-  // one per chunk (vector-memory counters complete in order).
-  u32x4 kreg[KPT], vreg[KPT];
-  int pbs[kKT / 16];
-  auto lookup_blocks = [&](int kt) {
-#pragma unroll
-    for (int j = 0; j < kKT / 16; ++j) pbs[j] = phys_block(bt_row, (kt >> 4) + j, n_lblocks, a.num_blocks);
-  };
-  // Chunk i of a thread holds key tid / (D/8) + i * (kThreads / (D/8)) of the tile; the key's
-  // block is wave-uniform, so K and V are read through one buffer resource per (block, KV
-  // head): a scalar base plus a loop-invariant lane offset, no address arithmetic per load.
-  // A block past the sequence or out of range gets zero records (its loads return zeros);
-  // V rows past the sequence end (last tile only) are read at an offset past the records.
+  // A wave's 64 lanes cover 64/(D/8) consecutive keys of one 16-token block, so chunk i of a
+  // wave lies in a block known from the wave index alone: each wave looks up only its own
+  // KPT block ids (scalar loads, same address in every lane) and reads K and V through one
+  // buffer resource per (block, KV head): a scalar base plus a loop-invariant lane offset.
+  // The loads go out together once the ids are back, so a tile costs one table round trip
+  // (vector-memory counters complete in order).  A block past the sequence or out of range
+  // gets zero records (its loads return zeros); V rows past the sequence end (last tile
+  // only) are read at an offset past the records.
   constexpr int kKeysPerRound = kThreads / (D / 8);     // keys covered by one round of chunks
-  auto load_kv = [&](int kt) {
-    const bool tail = kt + kKT > total;                // uniform: the tile holds the end
-    __amdgpu_buffer_rsrc_t rk[kKT / 16], rv[kKT / 16];
+  constexpr int kKeysPerWave = 64 / (D / 8);            // keys of one wave in one round
+  static_assert(16 % kKeysPerWave == 0 && kKeysPerRound % 16 == 0, "a wave's chunk stays in one block");
+  const int wave_key0 = __builtin_amdgcn_readfirstlane(wave) * kKeysPerWave;
+  const int lane_off = (((tid / (D / 8)) & 15) * D + 8 * (tid % (D / 8))) * 2;   // bytes
+  u32x4 kreg[KPT], vreg[KPT];
+  int pbs[KPT];
+  // Branch-free: the entry is read at min(lb, n_lblocks - 1) (n_lblocks >= 1 here) and
+  // discarded past the end, so the KPT scalar loads share one wait.
+  auto lookup_blocks = [&](int kt) {
+    int raw[KPT];
 #pragma unroll
-    for (int j = 0; j < kKT / 16; ++j) {
-      const int pb = pbs[j];
-      const size_t blk = ((size_t)(pb >= 0 ? pb : 0) * Hkv + g) * head_stride;
-      rk[j] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + blk), (short)0, pb >= 0 ? 32 * D : 0, 0x00020000);
-      rv[j] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + blk), (short)0, pb >= 0 ? 32 * D : 0, 0x00020000);
-    }
+    for (int i = 0; i < KPT; ++i)
+      raw[i] = bt_row[min((kt + wave_key0 + kKeysPerRound * i) >> 4, n_lblocks - 1)];
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int key = tid / (D / 8) + kKeysPerRound * i, dc = tid % (D / 8);
-      const int off = ((key & 15) * D + 8 * dc) * 2;      // bytes
-      const int j = __builtin_amdgcn_readfirstlane(key >> 4);
-      __amdgpu_buffer_rsrc_t ck = rk[0], cv = rv[0];
+      const int lb = (kt + wave_key0 + kKeysPerRound * i) >> 4;
+      pbs[i] = (lb < n_lblocks && raw[i] >= 0 && raw[i] < a.num_blocks) ? raw[i] : -1;
+    }
+  };
+  auto load_kv = [&](int kt) {
+    const bool tail = kt + kKT > total;                // uniform: the tile holds the end
 #pragma unroll
-      for (int q = 1; q < kKT / 16; ++q)
-        if (j == q) { ck = rk[q]; cv = rv[q]; }
-      kreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ck, off, 0, 0));
-      const int voff = (tail && kt + key >= total) ? (int)0x80000000 : off;
-      vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cv, voff, 0, 0));
+    for (int i = 0; i < KPT; ++i) {
+      const int pb = pbs[i];
+      const size_t blk = ((size_t)(pb >= 0 ? pb : 0) * Hkv + g) * head_stride;
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + blk), (short)0, pb >= 0 ? 32 * D : 0, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + blk), (short)0, pb >= 0 ? 32 * D : 0, 0x00020000);
+      const int key = tid / (D / 8) + kKeysPerRound * i;
+      kreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off, 0, 0));
+      const int voff = (tail && kt + key >= total) ? (int)0x80000000 : lane_off;
+      vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0));
     }
   };
   auto store_tile = [&](int buf) {
