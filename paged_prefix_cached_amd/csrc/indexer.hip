@@ -7,9 +7,9 @@
 // scale is positive, so it commutes with the ReLU and is applied once after the head sum.
 //
 // A workgroup of 8 waves owns 8 query rows (one per wave) and a chunk of keys.  Key
-// tiles of 64 tokens are gathered through the block table, upcast exactly from FP8 to
-// bf16 and staged in LDS once for all 8 queries (two buffers; the following tile's bytes
-// are in registers meanwhile).  Each wave keeps its query's 64 x 128 bf16 heads in
+// tiles of 64 tokens (one block each; the block id is read a tile ahead) are gathered
+// through the block table, upcast exactly from FP8 to bf16 and staged in LDS once for all
+// 8 queries (two buffers; the following tile's bytes are in registers meanwhile).  Each wave keeps its query's 64 x 128 bf16 heads in
 // registers (A operand) and computes C[heads x keys] with
 // v_mfma_f32_16x16x32_bf16: in the C layout a lane holds 4 heads of one key, so the
 // weighted ReLU head sum is 16 fused multiply-adds in registers plus a 2-step reduction
@@ -93,11 +93,23 @@ __global__ __launch_bounds__(512) void indexer_kernel(IndexerArgs a) {
     const int key = tid >> 3, dc = tid & 7;        // 64 keys x 128 B: one 16 B chunk a thread
     u32x4 raw = {0, 0, 0, 0};
     float rsc = 0.f;
-    auto load_tile = [&](int kb) {
+    // A 64-key tile is exactly one 64-token block.  Its table entry is read one tile ahead
+    // of its key loads (a vector load from an opaque copy of the index, so it is counted
+    // with the key loads, in order, and never waits alone): the key loads of a tile never
+    // wait for a table round trip.  Entries past the end are read clamped and discarded.
+    auto bt_raw = [&](int kb) -> int {
+      int lb = min(kb / kBs, n_lblocks - 1);
+      asm volatile("" : "+v"(lb));
+      return bt_row[lb];
+    };
+    auto bt_ok = [&](int kb, int raw_id) -> int {
+      return (kb / kBs < n_lblocks && raw_id >= 0 && raw_id < a.num_blocks) ? raw_id : -1;
+    };
+    auto load_tile = [&](int kb, int pb) {
       const int t = kb + key;
-      const int pb = t < total ? phys_block(bt_row, t / kBs, n_lblocks, a.num_blocks) : -1;
-      raw = pb >= 0 ? ld16(a.keys + ((size_t)pb * kBs + t % kBs) * kD + 16 * dc) : u32x4{0, 0, 0, 0};
-      if (dc == 0) rsc = pb >= 0 ? a.key_scale[(size_t)pb * kBs + t % kBs] : 0.f;
+      const bool ok = pb >= 0 && t < total;
+      raw = ok ? ld16(a.keys + ((size_t)pb * kBs + t % kBs) * kD + 16 * dc) : u32x4{0, 0, 0, 0};
+      if (dc == 0) rsc = ok ? a.key_scale[(size_t)pb * kBs + t % kBs] : 0.f;
     };
     auto store_tile = [&](int buf) {
       uint32_t bf[8];
@@ -112,18 +124,24 @@ __global__ __launch_bounds__(512) void indexer_kernel(IndexerArgs a) {
       st16(kp + 8, u32x4{bf[4], bf[5], bf[6], bf[7]});
       if (dc == 0) sc_s[buf][key] = rsc;
     };
-    if (c0 < kc_end) {
+    int id_next = -1;                                // raw table entry of tile tt+2
+    if (c0 < kc_end) {                               // (then n_lblocks >= 1)
       __syncthreads();                               // a previous sequence pass is done with LDS
-      load_tile(c0);
+      load_tile(c0, bt_ok(c0, bt_raw(c0)));
       store_tile(0);
-      if (c0 + kKT < kc_end) load_tile(c0 + kKT);
+      if (c0 + kKT < kc_end) load_tile(c0 + kKT, bt_ok(c0 + kKT, bt_raw(c0 + kKT)));
+      id_next = bt_raw(c0 + 2 * kKT);
       __syncthreads();
     }
     for (int kb = c0, tt = 0; kb < kc_end; kb += kKT, ++tt) {
       const int buf = tt & 1;
       if (kb + kKT < kc_end) {
         store_tile(buf ^ 1);                         // tile tt+1 (its loads went out last step)
-        if (kb + 2 * kKT < kc_end) load_tile(kb + 2 * kKT);
+        if (kb + 2 * kKT < kc_end) {
+          const int pb = bt_ok(kb + 2 * kKT, id_next);
+          load_tile(kb + 2 * kKT, pb);
+          id_next = bt_raw(kb + 3 * kKT);
+        }
       }
       if (mine && kb <= pos) {
 #pragma unroll
