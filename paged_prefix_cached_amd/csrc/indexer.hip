@@ -144,25 +144,35 @@ __global__ __launch_bounds__(512) void indexer_kernel(IndexerArgs a) {
         }
       }
       if (mine && kb <= pos) {
+        // all four 16-key sub-tiles in one basic block (the stores come after), so one
+        // sub-tile's MFMAs overlap the previous one's ReLU sums
+        float part[kKT / 16];
 #pragma unroll
         for (int st = 0; st < kKT / 16; ++st) {
           u32x4 kb4[4];
           const uint16_t* kp = k_s[buf] + (16 * st + m16) * kKStride + 8 * grp;
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) kb4[ks] = *reinterpret_cast<const u32x4*>(kp + 32 * ks);
-          float part = 0.f;
+          float acc = 0.f;
 #pragma unroll
           for (int ht = 0; ht < NHT; ++ht) {
             f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) c = mfma16x16x32(qa[ht][ks], kb4[ks], c);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) part = fmaf(wv[ht][r], fmaxf(c[r], 0.f), part);
+            for (int r = 0; r < 4; ++r) acc = fmaf(wv[ht][r], __builtin_amdgcn_fmed3f(c[r], 0.f, 3.402823466e38f), acc);   // ReLU (finite scores)
           }
-          part += __shfl_xor(part, 16);
-          part += __shfl_xor(part, 32);
+          // sum over the 4 lane groups (lanes l, l^16, l^32, l^48 hold the same key) with
+          // row swaps: every lane adds the same two operands, so all copies agree
+          const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
+          const float a16 = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+          const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a16), __float_as_uint(a16), false, false);
+          part[st] = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+        }
+#pragma unroll
+        for (int st = 0; st < kKT / 16; ++st) {
           const int t = kb + 16 * st + m16;
-          if (grp == 0 && t <= pos && t < c1) srow[t] = part * sc_s[buf][16 * st + m16] + 0.f;
+          if (grp == 0 && t <= pos && t < c1) srow[t] = part[st] * sc_s[buf][16 * st + m16] + 0.f;
         }
       }
       __syncthreads();
