@@ -82,7 +82,8 @@ typedef int pa_status;
  *     scale: dev fp32 [num_blocks][block_size], dequantised K_t = scale_t * e4m3(k_t).
  *   Indexer keys (kv_dtype PA_FP8_E4M3, block_size 64, num_kv_heads 1,
  *                 head_dim_qk 128, head_dim_v 0): k e4m3 [num_blocks][64][128] plus
- *     scale as above; they share the MLA block table. */
+ *     scale as above; they share the MLA block table.
+ *   FP8 pools: num_blocks * 64 must fit in int32 (PA_ERR_UNSUPPORTED otherwise). */
 typedef struct {
   int32_t num_blocks;
   int32_t block_size;

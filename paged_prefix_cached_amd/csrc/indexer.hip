@@ -21,7 +21,11 @@ namespace pa {
 namespace {
 
 constexpr int kD = 128, kBs = 64;
-constexpr int kWaves = 8;
+#ifndef PA_INDEXER_WAVES
+#define PA_INDEXER_WAVES 8
+#endif
+constexpr int kWaves = PA_INDEXER_WAVES;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kKT = 64;                  // keys per LDS tile
 constexpr int kChunk = 8192;             // keys per workgroup
 constexpr int kKStride = kD + 8;         // bf16 per key row in LDS (272 B)
@@ -36,7 +40,7 @@ __device__ __forceinline__ int find_seq(const int32_t* q_start, int num_seqs, in
 }
 
 template <int NHT>   // head tiles of 16 (num_heads / 16)
-__global__ __launch_bounds__(512) void indexer_kernel(IndexerArgs a) {
+__global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t k_s[2][kKT * kKStride];
   __shared__ float sc_s[2][kKT];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -90,9 +94,13 @@ __global__ __launch_bounds__(512) void indexer_kernel(IndexerArgs a) {
     // Tile pipeline, one barrier per tile: at the top of step t the FP8 bytes of tile t+1
     // (loaded during step t-1) are upcast into LDS buffer (t+1)&1, which the barrier
     // ending step t-1 freed; tile t+2's loads go out; tile t is computed from buffer t&1.
-    const int key = tid >> 3, dc = tid & 7;        // 64 keys x 128 B: one 16 B chunk a thread
-    u32x4 raw = {0, 0, 0, 0};
-    float rsc = 0.f;
+    // 64 keys x 128 B = 512 chunks of 16 B; chunk tid + kThreads j of a thread holds key
+    // (tid + kThreads j) / 8, bytes 16 (tid % 8) ..
+    constexpr int CPT = kKT * (kD / 16) / kThreads;
+    static_assert(CPT * kThreads == kKT * (kD / 16), "whole chunks per thread");
+    const int key = tid >> 3, dc = tid & 7;
+    u32x4 raw[CPT];
+    float rsc[CPT];
     // A 64-key tile is exactly one 64-token block.  Its table entry is read one tile ahead
     // of its key loads (a vector load from an opaque copy of the index, so it is counted
     // with the key loads, in order, and never waits alone): the key loads of a tile never
@@ -106,23 +114,30 @@ __global__ __launch_bounds__(512) void indexer_kernel(IndexerArgs a) {
       return (kb / kBs < n_lblocks && raw_id >= 0 && raw_id < a.num_blocks) ? raw_id : -1;
     };
     auto load_tile = [&](int kb, int pb) {
-      const int t = kb + key;
-      const bool ok = pb >= 0 && t < total;
-      raw = ok ? ld16(a.keys + ((size_t)pb * kBs + t % kBs) * kD + 16 * dc) : u32x4{0, 0, 0, 0};
-      if (dc == 0) rsc = ok ? a.key_scale[(size_t)pb * kBs + t % kBs] : 0.f;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int t = kb + key + (kThreads / 8) * j;
+        const bool ok = pb >= 0 && t < total;
+        raw[j] = ok ? ld16(a.keys + ((size_t)pb * kBs + t % kBs) * kD + 16 * dc) : u32x4{0, 0, 0, 0};
+        if (dc == 0) rsc[j] = ok ? a.key_scale[(size_t)pb * kBs + t % kBs] : 0.f;
+      }
     };
     auto store_tile = [&](int buf) {
-      uint32_t bf[8];
 #pragma unroll
-      for (int w4 = 0; w4 < 4; ++w4) {
-        const u32x2 c = fp8x4_to_bf16x4(raw[w4]);
-        bf[2 * w4] = c.x;
-        bf[2 * w4 + 1] = c.y;
+      for (int j = 0; j < CPT; ++j) {
+        uint32_t bf[8];
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+          const u32x2 c = fp8x4_to_bf16x4(raw[j][w4]);
+          bf[2 * w4] = c.x;
+          bf[2 * w4 + 1] = c.y;
+        }
+        const int kj = key + (kThreads / 8) * j;
+        uint16_t* kp = k_s[buf] + kj * kKStride + 16 * dc;
+        st16(kp, u32x4{bf[0], bf[1], bf[2], bf[3]});
+        st16(kp + 8, u32x4{bf[4], bf[5], bf[6], bf[7]});
+        if (dc == 0) sc_s[buf][kj] = rsc[j];
       }
-      uint16_t* kp = k_s[buf] + key * kKStride + 16 * dc;
-      st16(kp, u32x4{bf[0], bf[1], bf[2], bf[3]});
-      st16(kp + 8, u32x4{bf[4], bf[5], bf[6], bf[7]});
-      if (dc == 0) sc_s[buf][key] = rsc;
     };
     int id_next = -1;                                // raw table entry of tile tt+2
     if (c0 < kc_end) {                               // (then n_lblocks >= 1)
@@ -191,10 +206,10 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)((a.n_q + kWaves - 1) / kWaves) * n_chunks;
   if (grid == 0) return hipSuccess;
   switch (a.num_heads / 16) {
-    case 1: hipLaunchKernelGGL(indexer_kernel<1>, dim3(grid), dim3(512), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(indexer_kernel<2>, dim3(grid), dim3(512), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(indexer_kernel<3>, dim3(grid), dim3(512), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(indexer_kernel<4>, dim3(grid), dim3(512), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL(indexer_kernel<1>, dim3(grid), dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(indexer_kernel<2>, dim3(grid), dim3(kThreads), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(indexer_kernel<3>, dim3(grid), dim3(kThreads), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(indexer_kernel<4>, dim3(grid), dim3(kThreads), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -14,9 +14,10 @@
 // one query, each wave a quarter of the dimensions).
 // Keys go in 32-key tiles through a three-stage pipeline:
 //   1. LDS-DMA (global_load_lds, 16 bytes a lane) gathers tile t+2's FP8 rows through the
-//      block table into a raw LDS buffer -- no registers held while the loads fly.  Block
-//      ids (decode: the split's range; sparse: the sequence's row) and, for sparse, the
-//      selected positions are staged in LDS once.
+//      block table into a raw LDS buffer -- no registers held while the loads fly.  Decode
+//      stages its range's block ids in LDS once; sparse resolves every selected position
+//      to its physical row (block * 64 + offset) once and stages the rows, so the DMA of
+//      a tile waits for no table lookup.
 //   2. All threads upcast tile t+1's raw bytes once, exactly, to fp16 into a row-major
 //      LDS tile (16-byte chunks XOR-swizzled by row/4: conflict-free for both read
 //      patterns below); keys that are invalid (past the range, unselected, bad block id)
@@ -48,7 +49,6 @@ constexpr int kKT = 32;                   // keys per tile
 constexpr int kKS = 608;                  // fp16 per LDS row: 1,216 B, 304 dwords = 48 mod 64
 constexpr int kChunks = kKT * (kDqk / 16);   // 16-byte FP8 chunks per tile (1,152)
 constexpr int kWaveLoads = kChunks / 64;     // 1 KB DMA wave-loads per tile (18)
-constexpr int kBtLds = 4096;              // block-table entries staged in LDS (sparse)
 constexpr int kSelLds = 2048;             // selected positions staged in LDS (sparse)
 static_assert(kChunks % 64 == 0, "tile is a whole number of wave-loads");
 static_assert(kKS >= kDqk + 16, "row 0's padding takes the discarded chunk slots");
@@ -99,10 +99,9 @@ __device__ __forceinline__ void barrier_lds() {
 
 // NW waves per workgroup; SPLIT waves share each group of 32 query rows (1: a wave holds
 // all 576 Q dims and all 512 output dims; 2 or 4: the waves split both, exchanging
-// partial S through LDS).  STAGED (sparse only): the selected positions (k <= 2048) and the
-// sequence's block-table row (<= 4096 entries) are copied to LDS once; otherwise they
-// are read from global memory (a separate instantiation, so no lookup ever becomes a
-// flat access).  LATE_CONV: the upcast of tile t+1 runs interleaved with the P.V of tile
+// partial S through LDS).  STAGED (sparse only): the physical rows of the selections
+// (k <= 2048) are resolved once and kept in LDS; otherwise every tile resolves its keys
+// from global memory (a separate instantiation, so no lookup ever becomes a flat access).  LATE_CONV: the upcast of tile t+1 runs interleaved with the P.V of tile
 // t (pays off with one wave a SIMD and registers to spare) instead of at the start of
 // step t.
 template <bool SPARSE, int NW, int SPLIT, bool STAGED, bool LATE_CONV>
@@ -127,9 +126,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
   __shared__ __attribute__((aligned(16))) float fvs[2][kKT];     // scale
   __shared__ int32_t fall[2];                                    // 1: every key of the tile valid
   __shared__ __attribute__((aligned(16))) f32x4 xs[SPLIT > 1 ? NW * 4 * 64 : 1];  // partial S
-  // eight-wave sparse workgroups stage only the selections (their LDS holds no block table)
-  constexpr bool STAGE_BT = STAGED && NW <= 4;
-  __shared__ int32_t bt_s[SPARSE ? (STAGE_BT ? kBtLds : 1) : kDecodeSplitMla / kBs + 1];
+  // decode stages its range's block ids; sparse stages, per selection, the physical row
+  // (block * 64 + offset, or -1) resolved through the block table once per workgroup
+  __shared__ int32_t bt_s[SPARSE ? 1 : kDecodeSplitMla / kBs + 1];
   __shared__ int32_t sel_s[SPARSE && STAGED ? kSelLds : 1];
   // Decode (two waves a SIMD) keeps its first Q fragment in LDS, one 16-byte read per tile,
   // instead of a register: the register file is the limit there, and a spilled fragment
@@ -166,7 +165,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
     sel_g = sa.topk + (size_t)i * sa.k;
     n_keys = sa.k;
     n_lblocks = sa.bt_stride;
-    n_bt = STAGE_BT ? sa.bt_stride : 0;
+    n_bt = 0;
     scale_log2 = sa.scale_log2;
   } else {
     Hq = da.num_q_heads;
@@ -215,32 +214,24 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
     }
   }
 
-  // ---- stage validated block ids and, for sparse, the selected positions
+  // ---- stage validated block ids (decode) or the selections' physical rows (sparse)
+  // j-th selection -> physical row of the pool (block * 64 + offset), -1 if unselected or
+  // its block id is out of range (rows fit in 32 bits: the library checks num_blocks)
+  auto sel_row = [&](int idx) -> int {
+    if (idx < 0) return -1;
+    const int pb = phys_block(bt_row, idx / kBs, n_lblocks, num_blocks);
+    return pb >= 0 ? pb * kBs + idx % kBs : -1;
+  };
   for (int j = tid; j < n_bt; j += NT) bt_s[j] = phys_block(bt_row, lb_base + j, n_lblocks, num_blocks);
   if constexpr (SPARSE && STAGED) {
-    for (int j = tid; j < n_keys; j += NT) sel_s[j] = sel_g[j];
+    for (int j = tid; j < n_keys; j += NT) sel_s[j] = sel_row(sel_g[j]);
   }
   __syncthreads();
-  // j-th key of the unit -> physical block (or -1) and its logical position
-  auto key_loc = [&](int j, int& idx) -> int {
-    idx = -1;
+  // sparse: j-th key of the unit -> physical row, or -1
+  auto key_row = [&](int j) -> int {
     if (j >= n_keys) return -1;
-    if constexpr (SPARSE) {
-      if constexpr (STAGED) {
-        idx = sel_s[j];
-        if (idx < 0) return -1;
-        const int lb = idx / kBs;
-        if constexpr (!STAGE_BT) return phys_block(bt_row, lb, n_lblocks, num_blocks);
-        return lb < n_bt ? bt_s[lb] : -1;
-      } else {
-        idx = sel_g[j];
-        if (idx < 0) return -1;
-        return phys_block(bt_row, idx / kBs, n_lblocks, num_blocks);
-      }
-    } else {
-      idx = k_begin + j;
-      return bt_s[idx / kBs - lb_base];
-    }
+    if constexpr (STAGED) return sel_s[j];
+    else return sel_row(sel_g[j]);
   };
 
   // ---- stage 1: DMA tile tt into raw buffer P.  Raw chunk c (16 bytes: key c / 36,
@@ -269,25 +260,24 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
         RK[ln] = (pb >= 0 && kb + ln < n_keys) ? pos0 + ln : -1;
       }
     } else {
-      // per-key lookups, all LDS reads issued before the DMAs
-      int idx[kLoadsPerWave], pbk[kLoadsPerWave];
+      // per-key rows, all LDS reads issued before the DMAs; a valid key's RK entry is its
+      // physical row (>= 0: the only property the sparse path reads)
+      int prow[kLoadsPerWave];
 #pragma unroll
       for (int m = 0; m < kLoadsPerWave; ++m) {
         const int key = (64 * (wave + NW * m) + ln) / (kDqk / 16);
-        pbk[m] = key_loc(kb + key, idx[m]);
+        prow[m] = key_row(kb + key);
       }
 #pragma unroll
       for (int m = 0; m < kLoadsPerWave; ++m) {
         const int j = wave + NW * m;
         const int dc = (64 * j + ln) % (kDqk / 16);
-        if (j < kWaveLoads)
-          dma16(pbk[m] >= 0 ? kv + ((size_t)pbk[m] * kBs + idx[m] % kBs) * kDqk + 16 * dc : kv, lds_u32(R) + 1024 * j);
+        if (j < kWaveLoads) dma16(prow[m] >= 0 ? kv + (size_t)prow[m] * kDqk + 16 * dc : kv, lds_u32(R) + 1024 * j);
       }
       if (wave == NW - 1 && ln < kKT) {
-        int id;
-        const int pb = key_loc(kb + ln, id);
-        dma4(pb >= 0 ? kv_scale + (size_t)pb * kBs + id % kBs : kv_scale, lds_u32(RS));
-        RK[ln] = pb >= 0 ? id : -1;
+        const int pr = key_row(kb + ln);
+        dma4(pr >= 0 ? kv_scale + pr : kv_scale, lds_u32(RS));
+        RK[ln] = pr;
       }
     }
   };
@@ -657,7 +647,7 @@ hipError_t launch_sparse_mla(const SparseMlaArgs& a, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   MlaDecodeArgs none{};
   if constexpr (kSparseStage) {
-    if (a.k <= kSelLds && (kSparseWaves > 4 || a.bt_stride <= kBtLds)) {
+    if (a.k <= kSelLds) {
       hipLaunchKernelGGL((mla_kernel<true, kSparseWaves, kSparseSplit, true, true>), dim3(grid), dim3(64 * kSparseWaves), 0,
                          stream, none, a);
       return hipGetLastError();

@@ -52,6 +52,7 @@ pa_status check_fp8_pool(const pa_kv_pool* p, int d_qk, int d_v, const char* wha
     return fail(PA_ERR_UNSUPPORTED, "%s pool head dims must be %d/%d (got %d/%d)", what, d_qk, d_v,
                 p->head_dim_qk, p->head_dim_v);
   if (p->num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  if (p->num_blocks > INT32_MAX / 64) return fail(PA_ERR_UNSUPPORTED, "%s pool: num_blocks * 64 rows must fit in int32", what);
   if (p->k == nullptr || p->scale == nullptr) return fail(PA_ERR_INVALID_ARG, "%s pool k/scale is NULL", what);
   if (!aligned(p->k, 16) || !aligned(p->scale, 4)) return fail(PA_ERR_INVALID_ARG, "%s pool must be 16-byte aligned", what);
   return PA_OK;

@@ -119,3 +119,13 @@ def test_indexer_and_sparse_validation(lib):
                                None, 0, None) == 2
     assert lib.sparse_mla_attn(FAKE, ctypes.byref(mp), FAKE, 10, FAKE, None, 4, 2048, 64, 0.04, FAKE, None,
                                None, 0, None) == 1
+
+
+def test_fp8_pool_rows_fit_int32(lib):
+    """The MLA kernels address FP8 pool rows (block * 64 + offset) in 32 bits."""
+    big = pa.KVPool(2**31 // 64, 64, 1, 576, 512, 2, FAKE, None, FAKE)
+    assert lib.sparse_mla_attn(FAKE, ctypes.byref(big), FAKE, 10, FAKE, FAKE, 4, 2048, 64, 0.04, FAKE, None,
+                               None, 0, None) == 2
+    ok = pa.KVPool(2**31 // 64 - 1, 64, 1, 576, 512, 2, FAKE, None, FAKE)
+    assert lib.sparse_mla_attn(FAKE, ctypes.byref(ok), FAKE, 10, FAKE, FAKE, 0, 2048, 64, 0.04, FAKE, None,
+                               None, 0, None) == 0

@@ -202,3 +202,31 @@ def test_sparse_mla_k_covers_context_equals_dense(pa_lib):
     torch.cuda.synchronize()
     (ro, _), _, _ = _mla_ref(mla, 0)
     assert_close(bf16_out(out), ro, FP8_MAX_ABS, FP8_L1, "sparse == dense")
+
+
+@pytest.mark.parametrize("k", [100, 2500])
+def test_sparse_mla_given_selection(pa_lib, k):
+    """Selections handed in directly, in random order with -1 holes: k <= 2,048 takes the
+    path with the selections' rows staged in LDS, k > 2,048 the one that resolves each
+    tile's rows from global memory.  A row with no selection at all gives zeros."""
+    import torch
+    n = 24
+    mla, idx = W.make_sparse_mla(93, lengths=[3000 + n], n_new=[n], num_q_heads=64)
+    dev = MlaOnDevice(mla, idx)
+    rng = np.random.default_rng(1000 + k)
+    pos = mla.q_pos(0)
+    tk = np.full((n, k), -1, np.int32)
+    for r in range(n - 1):                      # the last row keeps no selection
+        m = min(k, int(pos[r]) + 1) - int(rng.integers(0, 7))
+        tk[r, :m] = rng.choice(int(pos[r]) + 1, size=m, replace=False)
+        tk[r] = rng.permutation(tk[r])          # holes anywhere
+    topk = torch.from_numpy(tk).cuda()
+    out = pa_lib.sparse_mla_attn(dev.q, dev.pool, dev.bt, dev.q_seq, topk, scale=mla.scale)
+    torch.cuda.synchronize()
+    got = bf16_out(out)
+    L = int(mla.total_len[0])
+    codes = oracle.gather_paged(mla.kv_pool, mla.block_table[0], L)
+    sc = oracle.gather_paged(mla.kv_scale[..., None], mla.block_table[0], L)[:, 0]
+    ro, _ = oracle.sparse_mla_attention(mla.q[0:n], codes, sc, tk, mla.scale)
+    assert_close(got, ro, FP8_MAX_ABS, FP8_L1, f"sparse given selection k={k}")
+    assert np.all(got[n - 1] == 0)
