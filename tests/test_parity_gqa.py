@@ -195,7 +195,7 @@ def test_prefill_cold_prompt_full_size_sampled(pa_lib):
 
 def test_prefill_split_k_long_contexts(pa_lib):
     """Few, short new-token tiles over long contexts: the prefill splits each tile's keys
-    into 16,384-key ranges and merges the partials in a fixed order (decode tokens and
+    into 8,192-key ranges and merges the partials in a fixed order (decode tokens and
     prefill chunks in one call)."""
     wl = W.make_chunked_mixed(9, n_chunked=2, chunk=100, n_decode=3, lo=40000, hi=70000,
                               num_q_heads=8, num_kv_heads=2, head_dim=128, keep_content=True)
