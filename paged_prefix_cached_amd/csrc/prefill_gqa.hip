@@ -74,7 +74,8 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
   // tiles of one (sequence, key range) run together on one XCD (shared K/V in its L2);
   // the KV head varies slowest, so the XCDs split the work by head and a long sequence
   // is spread over all of them
-  const int tile = logical % n_tiles;
+  // unsplit, a later tile sees more keys (causal): the longest tiles are dealt first
+  const int tile = a.split_len > 0 ? logical % n_tiles : n_tiles - 1 - logical % n_tiles;
   const int split = (logical / n_tiles) % n_split;
   const int s = (logical / (n_tiles * n_split)) % a.num_seqs;
   const int g = logical / (n_tiles * n_split * a.num_seqs);
