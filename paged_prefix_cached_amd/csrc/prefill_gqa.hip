@@ -186,16 +186,19 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
     const uint16_t* kt_s = sm.k[buf];
     const uint16_t* vt_s = sm.v[buf];
     // ---- S^T = K Q^T, 32-key sub-tiles
+    // k-step outer, sub-tile inner: consecutive MFMAs accumulate into different tiles and
+    // each k-step's K reads have the previous k-step's kST MFMAs to land behind
     f32x16 sacc[kST];
 #pragma unroll
-    for (int st = 0; st < kST; ++st) {
+    for (int st = 0; st < kST; ++st)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[st][i] = 0.f;
-      const uint16_t* kp = kt_s + (32 * st + c32) * Sm::kStride + 8 * h32;
+    const uint16_t* kp = kt_s + c32 * Sm::kStride + 8 * h32;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        sacc[st] = mfma32x32x16(*reinterpret_cast<const u32x4*>(kp + 16 * ks), qb[ks], sacc[st]);
-    }
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int st = 0; st < kST; ++st)
+        sacc[st] = mfma32x32x16(*reinterpret_cast<const u32x4*>(kp + 32 * st * Sm::kStride + 16 * ks), qb[ks], sacc[st]);
     // ---- causal mask (diagonal tiles only) and the row maximum on raw scores
     float mx = -INFINITY;
     if (kt + kKT - 1 > wave_min_pos) {
