@@ -413,11 +413,24 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
     f32x16 s;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    if constexpr (SPARSE) {
+      // registers to spare here: every K fragment is read before the MFMAs, so the reads
+      // are in flight together instead of two at a time
+      u32x4 kf[kQW];
 #pragma unroll
-    for (int k = 0; k < kQW; ++k) {
-      const int ks = kQW * half + k;             // bases swapped above when kQW * half is odd
-      const uint16_t* kp = F + ((k & 1) ? k_odd : k_even) + 16 * ks;
-      s = mfma32x32x16_f16(*reinterpret_cast<const u32x4*>(kp), k < kQL ? qls[k * NT + tid] : qb[k], s);
+      for (int k = 0; k < kQW; ++k)
+        kf[k] = *reinterpret_cast<const u32x4*>(F + ((k & 1) ? k_odd : k_even) + 16 * (kQW * half + k));
+#pragma unroll
+      for (int k = 0; k < kQW; ++k) s = mfma32x32x16_f16(kf[k], k < kQL ? qls[k * NT + tid] : qb[k], s);
+      __builtin_amdgcn_sched_group_barrier(0x100, kQW, 0);   // the K reads first
+      __builtin_amdgcn_sched_group_barrier(0x008, kQW, 0);   // then the MFMAs
+    } else {
+#pragma unroll
+      for (int k = 0; k < kQW; ++k) {
+        const int ks = kQW * half + k;             // bases swapped above when kQW * half is odd
+        const uint16_t* kp = F + ((k & 1) ? k_odd : k_even) + 16 * ks;
+        s = mfma32x32x16_f16(*reinterpret_cast<const u32x4*>(kp), k < kQL ? qls[k * NT + tid] : qb[k], s);
+      }
     }
     return s;
   };
