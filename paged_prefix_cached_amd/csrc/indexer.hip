@@ -9,11 +9,13 @@
 // A workgroup of 8 waves owns 8 query rows (one per wave) and a chunk of keys.  Key
 // tiles of 64 tokens (one block each; the block id is read a tile ahead) are gathered
 // through the block table, upcast exactly from FP8 to bf16 and staged in LDS once for all
-// 8 queries (two buffers; the following tile's bytes are in registers meanwhile).  Each wave keeps its query's 64 x 128 bf16 heads in
-// registers (A operand) and computes C[heads x keys] with
-// v_mfma_f32_16x16x32_bf16: in the C layout a lane holds 4 heads of one key, so the
-// weighted ReLU head sum is 16 fused multiply-adds in registers plus a 2-step reduction
-// across the 4 lane groups.
+// 8 queries (two buffers; the following tile's bytes are in registers meanwhile).  Each
+// wave keeps its query's 64 x 128 bf16 heads in registers (A operand) and computes
+// C[heads x keys] with v_mfma_f32_16x16x32_bf16: in the C layout a lane holds 4 heads of
+// one key, so the weighted ReLU head sum is 16 fused multiply-adds in registers (ReLU as
+// one v_med3_f32) plus a 2-step reduction across the 4 lane groups (row swaps).  The four
+// 16-key sub-tiles of a tile form one basic block, their score stores after it, so one
+// sub-tile's MFMAs overlap the previous one's head sums.
 #include "pa_device.h"
 #include "pa_internal.h"
 

@@ -27,7 +27,11 @@
 // V (D + 32) fp16 (D/2 + 16 dwords, 16 or 48 mod 64: the 4 rows of a transpose read
 // phase hit distinct banks).
 // Workgroups of the same (sequence, KV head) are mapped onto one XCD so its L2 serves
-// the shared prefix to all of them; the XCDs take different KV heads.
+// the shared prefix to all of them; the XCDs take different KV heads.  Without a split,
+// the latest tiles are dealt first (under the causal mask they see the most keys).
+// Split-K (prefill_split_len): when the tiles alone cannot fill the GPU and the contexts
+// are long, each workgroup takes one key range of its tile and writes fp32 partials
+// (o, log2-sum-exp) that the decode combine kernel merges in range order.
 #include "pa_device.h"
 #include "pa_internal.h"
 
