@@ -60,6 +60,9 @@ def test_mla_decode(pa_lib, T, Hq):
         (ro, rl), _, _ = _mla_ref(mla, s)
         assert_close(got[s * T:(s + 1) * T], ro, FP8_MAX_ABS, FP8_L1, f"mla T={T} Hq={Hq} L={lengths[s]}")
         np.testing.assert_allclose(lg[s * T:(s + 1) * T], rl, atol=LSE_ABS)
+    # splits merged in a fixed order: a rerun is bit-identical
+    out2, lse2 = _mla_decode(pa_lib, dev, T)
+    assert bf16_out(out2).tobytes() == bf16_out(out).tobytes() and np.array_equal(lse2.cpu().numpy(), lse.cpu().numpy())
 
 
 def test_mla_decode_peaked(pa_lib):
