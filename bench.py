@@ -8,13 +8,20 @@ token, 32 query / 8 KV heads, head dim 128, bf16 K/V in a shuffled 16-token bloc
 contexts log-uniform in [4,000, 142,000], sequences in 8 sessions whose first 90% of
 blocks are shared (same physical blocks).  Inputs are resident in HBM before timing.
 
-Prints one JSON line.  `value` is decode KV throughput in GB/s counting each sequence's
-context (logical bytes: 4,096 B per token over the 8 KV heads, K+V, bf16).  The
-roofline object uses the algorithmic HBM bytes (each distinct KV block once, plus q and
-out) per launch over the decode kernel's average duration, timed with HIP events on the
-launch stream.  `cpu_baseline` times the CPU oracle (oracle/) on a bounded sample of the
-same batch.  `secondary` holds the other workloads (suffix prefill, MLA MTP3 decode,
-indexer + top-k + sparse MLA) when requested.
+Timing: W untimed warm-up steps, then K timed steps; before every step a 1 GiB
+device-to-device copy evicts L2 and the MALL (so reuse within a call counts, reuse across
+calls does not), and HIP events on the launch stream time each step alone.  ms_per_step
+is the median step; the minimum and mean are reported beside it, and the library's own
+events time each kernel launch.
+
+Prints one JSON line.  `value` is the step's algorithmic HBM throughput: the bytes the
+method must move (every distinct KV block once, 4,096 B per token over the 8 KV heads,
+K+V, bf16, plus q and out) over the median step time.  `effective_kv_gbps` counts each
+sequence's whole context instead (shared prefix blocks once per sequence).  The roofline
+object uses the same algorithmic bytes over the decode kernel's average launch time.
+`cpu_baseline` times the CPU oracle (oracle/) on the same batch with a process pool over
+the sequences, one single-threaded process per host core.  `secondary` holds the other
+workloads (suffix prefill, MLA MTP3 decode, indexer + top-k + sparse MLA by default).
 """
 from __future__ import annotations
 
@@ -22,7 +29,6 @@ import argparse
 import json
 import math
 import os
-import resource
 import sys
 import time
 
@@ -43,32 +49,66 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def _cpu_rusage():
-    r = resource.getrusage(resource.RUSAGE_SELF)
-    return r.ru_utime + r.ru_stime
+_FLUSH = []
 
 
-def timed_steps(step, steps, warmup, kernel=None):
-    """Run warmup + timed steps; returns (wall ms per step, avg ms of `kernel` launches)."""
+def _flush():
+    """Evict L2 and the MALL (256 MB) between timed steps: a 1 GiB device copy, on the
+    launch stream, outside the timed events."""
+    import torch
+    if not _FLUSH:
+        _FLUSH.append(torch.ones(1 << 30, dtype=torch.uint8, device="cuda"))
+        _FLUSH.append(torch.empty(1 << 30, dtype=torch.uint8, device="cuda"))
+    _FLUSH[1].copy_(_FLUSH[0])
+
+
+def timed_steps(step, steps, warmup):
+    """W warm-up steps, then `steps` timed steps, each after a cache flush.  Returns a dict:
+    median / min / mean ms per step (HIP events around each step on the launch stream),
+    wall ms per step including the flushes, and per-kernel launch times (ms) recorded by
+    the library's own events: {name: {"mean", "median", "min", "n"}}."""
     import torch
     import paged_prefix_cached_amd as pa
     for _ in range(warmup):
+        _flush()
         step()
     torch.cuda.synchronize()
     pa.pa_profile_enable(64 * max(1, steps))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(steps):
+        _flush()
+        ev[i][0].record()
         step()
+        ev[i][1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    per_step = np.array([a.elapsed_time(b) for a, b in ev])
     recs = pa.pa_profile_records()
     pa.pa_profile_disable()
     per_kernel = {}
     for name, ms in recs:
         per_kernel.setdefault(name, []).append(ms)
-    avg = {k: float(np.mean(v)) for k, v in per_kernel.items()}
-    return (t1 - t0) * 1e3 / steps, avg
+    kern = {k: {"mean": float(np.mean(v)), "median": float(np.median(v)), "min": float(np.min(v)), "n": len(v)}
+            for k, v in per_kernel.items()}
+    return {"ms": float(np.median(per_step)), "ms_min": float(per_step.min()), "ms_mean": float(per_step.mean()),
+            "wall_ms_incl_flush": (t1 - t0) * 1e3 / steps, "kernels": kern}
+
+
+def _kmean(t, name):
+    return t["kernels"].get(name, {}).get("mean", float("nan"))
+
+
+def _kms(t):
+    return {k: v["mean"] for k, v in t["kernels"].items()}
+
+
+def _mfma_roof(flops, k_ms, kernel, per_unit, peak=None):
+    peak = BF16_PEAK_TFLOPS if peak is None else peak
+    ach = flops / (k_ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
+            "traffic": None, "kernel": kernel, "flop_per_launch": flops, "per_unit": per_unit}
 
 
 def measured_traffic(counters_file: str, sources: list[str]):
@@ -112,13 +152,14 @@ def decode_bytes(wl):
     return unique, logical, qo
 
 
-def bench_decode(args, dev_name, share=True):
+def bench_decode(args, dev_name, wl=None, share=True):
     import torch
     import paged_prefix_cached_amd as pa
     import workloads as W
     from workloads.device import GqaOnDevice
     t = time.time()
-    wl = W.make_gqa_decode(2, share=share)
+    if wl is None:
+        wl = W.make_gqa_decode(2, share=share)
     dev = GqaOnDevice(wl)
     log(f"[bench] decode workload ready in {time.time() - t:.1f}s")
     S, H, D = wl.num_seqs, wl.num_q_heads, wl.head_dim
@@ -131,16 +172,22 @@ def bench_decode(args, dev_name, share=True):
         pa.paged_attn_decode(q, dev.pool, dev.bt, dev.total_len, q_per_seq=1, num_q_heads=H,
                              max_context_len=dev.max_total, scale=wl.scale, out=out, workspace=ws)
 
-    ms, kern = timed_steps(step, args.steps, args.warmup)
+    tm = timed_steps(step, args.steps, args.warmup)
     unique, logical, qo = decode_bytes(wl)
-    k_ms = kern.get("decode_gqa", float("nan"))
+    ms = tm["ms"]
+    k_ms = _kmean(tm, "decode_gqa")
     algo = unique + qo
     res = {
         "ms_per_step": ms,
-        "value": logical / (ms * 1e-3) / 1e9,
-        "unique_kv_gbps": unique / (ms * 1e-3) / 1e9,
+        "ms_per_step_min": tm["ms_min"],
+        "ms_per_step_mean": tm["ms_mean"],
+        "wall_ms_per_step_incl_flush": tm["wall_ms_incl_flush"],
+        "value": algo / (ms * 1e-3) / 1e9,
+        "effective_kv_gbps": logical / (ms * 1e-3) / 1e9,
         "tokens_per_s": S / (ms * 1e-3),
-        "kernel_ms": kern,
+        "kernel_ms": _kms(tm),
+        "kernel_ms_median": {k: v["median"] for k, v in tm["kernels"].items()},
+        "workspace_bytes": nws,
         "roofline": {"bound": "hbm", "achieved": algo / (k_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": algo / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "traffic": measured_traffic("gqa_decode_kernel.hbm-counters.decode-64seq.txt", DECODE_SOURCES)
@@ -157,56 +204,68 @@ def bench_decode(args, dev_name, share=True):
     return res, wl
 
 
-def cpu_baseline(wl, budget_s: float):
-    """Time the CPU oracle on the first sequences of the decode batch (bounded)."""
+# ---- CPU oracle baseline: a process pool over the decode sequences (forked before the
+# GPU is touched, so the workers hold no device state); each worker single-threaded.
+_CPU_WL = None
+
+
+def _cpu_one(s):
     import oracle
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        oracle.paged_gqa_attention(_CPU_WL, s)
+    return s
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, budget_s: float):
+    """Time the CPU oracle on the decode batch: one process per host core, each taking
+    whole sequences as they finish, stopped once `budget_s` of wall time has passed.  The rate
+    counts the sample's distinct KV bytes (shared blocks once), like the GPU's value."""
+    import multiprocessing as mp
+    global _CPU_WL
+    _CPU_WL = wl
+    ncores = len(os.sched_getaffinity(0))
     per_tok = wl.num_kv_heads * wl.head_dim * 2 * 2
-    done_bytes, n = 0, 0
-    c0, t0 = _cpu_rusage(), time.perf_counter()
-    order = list(range(wl.num_seqs))
-    for s in order:
-        oracle.paged_gqa_attention(wl, s)
-        done_bytes += int(wl.total_len[s]) * per_tok
-        n += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    done = []
+    with ctx.Pool(ncores) as pool:
+        for s in pool.imap_unordered(_cpu_one, range(wl.num_seqs)):
+            done.append(s)
+            if time.perf_counter() - t0 > budget_s:
+                pool.terminate()
+                break
     wall = time.perf_counter() - t0
-    cpu = _cpu_rusage() - c0
-    return {"value": done_bytes / wall / 1e9, "unit": "GB/s", "cores": max(1, int(round(cpu / wall))),
-            "kind": "oracle",
-            "sample": f"first {n} of {wl.num_seqs} decode sequences ({done_bytes / 4096:.0f} context tokens), "
-                      f"{wall:.1f} s wall, {cpu:.1f} s CPU",
-            "host_threads_available": len(os.sched_getaffinity(0))}
+    seen = {}
+    for s in done:
+        L = int(wl.total_len[s])
+        for j in range(-(-L // 16)):
+            b = int(wl.block_table[s, j])
+            seen[b] = max(seen.get(b, 0), min(16, L - 16 * j))
+    distinct = sum(seen.values()) * per_tok + len(done) * wl.num_q_heads * wl.head_dim * 4
+    logical = int(sum(int(wl.total_len[s]) for s in done)) * per_tok
+    return {"value": distinct / wall / 1e9, "unit": "GB/s", "cores": ncores, "kind": "oracle",
+            "sample": f"{len(done)} of {wl.num_seqs} decode sequences ({logical // per_tok} context tokens, "
+                      f"{distinct / 1e9:.2f} GB distinct), {wall:.1f} s wall on {ncores} single-threaded "
+                      f"fp64 numpy processes",
+            "effective_kv_gbps": logical / wall / 1e9, "cpu_model": _cpu_model()}
 
 
 # --------------------------------------------------------------------------- secondary workloads
-def bench_prefill(steps, warmup):
-    import torch
-    import paged_prefix_cached_amd as pa
-    import workloads as W
-    from workloads.device import GqaOnDevice
-    t = time.time()
-    wl = W.make_prefix_prefill(3)
-    dev = GqaOnDevice(wl)
-    del wl.k_pool, wl.v_pool
-    log(f"[bench] prefill workload ready in {time.time() - t:.1f}s")
-    out = torch.empty((wl.q.shape[0], wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
-
-    def step():
-        pa.paged_attn_prefill(dev.q, dev.pool, dev.bt, dev.cached, dev.n_new, dev.q_start,
-                              num_q_heads=wl.num_q_heads, max_new_len=dev.max_new,
-                              max_total_len=dev.max_total, scale=wl.scale, out=out)
-
-    ms, kern = timed_steps(step, steps, warmup)
+def _prefill_flops(wl):
     pairs = sum(int(c) * int(n) + int(n) * (int(n) + 1) // 2
                 for c, n in zip(wl.total_len - wl.n_new, wl.n_new))
-    flops = pairs * wl.num_q_heads * 4 * wl.head_dim
-    k_ms = kern.get("prefill_gqa", float("nan"))
-    return {"workload": "prefix-cached suffix prefill: 8 seqs x (142000 cached + 2048 new), 32q/8kv, d128, bf16",
-            "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12, "tokens_per_s": wl.q.shape[0] / (ms * 1e-3),
-            "kernel_ms": kern, "flop": flops,
-            "roofline": {"bound": "mfma", "achieved": flops / (k_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": flops / (k_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}}
+    return pairs * wl.num_q_heads * 4 * wl.head_dim
 
 
 def _bench_gqa_prefill_workload(wl, label, steps, warmup):
@@ -224,15 +283,22 @@ def _bench_gqa_prefill_workload(wl, label, steps, warmup):
                               num_q_heads=wl.num_q_heads, max_new_len=dev.max_new,
                               max_total_len=dev.max_total, scale=wl.scale, out=out)
 
-    ms, kern = timed_steps(step, steps, warmup)
-    pairs = sum(int(c) * int(n) + int(n) * (int(n) + 1) // 2
-                for c, n in zip(wl.total_len - wl.n_new, wl.n_new))
-    flops = pairs * wl.num_q_heads * 4 * wl.head_dim
-    k_ms = kern.get("prefill_gqa", float("nan"))
-    return {"workload": label, "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
-            "tokens_per_s": wl.q.shape[0] / (ms * 1e-3), "kernel_ms": kern, "flop": flops,
-            "roofline": {"bound": "mfma", "achieved": flops / (k_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": flops / (k_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}}
+    tm = timed_steps(step, steps, warmup)
+    flops = _prefill_flops(wl)
+    ms = tm["ms"]
+    return {"workload": label, "ms": ms, "ms_min": tm["ms_min"], "tflops": flops / (ms * 1e-3) / 1e12,
+            "tokens_per_s": wl.q.shape[0] / (ms * 1e-3), "kernel_ms": _kms(tm), "flop": flops,
+            "roofline": _mfma_roof(flops, _kmean(tm, "prefill_gqa"), "gqa_prefill_kernel",
+                                   "4 x 128 FLOP per (query head, visible key)")}
+
+
+def bench_prefill(steps, warmup):
+    import workloads as W
+    t = time.time()
+    wl = W.make_prefix_prefill(3)
+    log(f"[bench] prefill workload ready in {time.time() - t:.1f}s")
+    return _bench_gqa_prefill_workload(
+        wl, "prefix-cached suffix prefill: 8 seqs x (142000 cached + 2048 new), 32q/8kv, d128, bf16", steps, warmup)
 
 
 def bench_cold(steps, warmup):
@@ -281,19 +347,18 @@ def bench_chunked(steps, warmup):
         pa.paged_attn_decode(d_q, pool, d_bt, d_ctx, q_per_seq=1, num_q_heads=wl.num_q_heads,
                              max_context_len=max_ctx, scale=wl.scale, out=out_d, workspace=ws)
 
-    ms, kern = timed_steps(step, steps, warmup)
+    tm = timed_steps(step, steps, warmup)
     pairs = sum(int(c) * int(n) + int(n) * (int(n) + 1) // 2 for c, n in zip(cached[:nc], wl.n_new[:nc]))
     flops = pairs * wl.num_q_heads * 4 * wl.head_dim
     kv_bytes = int(wl.total_len[nc:].astype(np.int64).sum()) * wl.num_kv_heads * wl.head_dim * 4
-    k_ms = kern.get("prefill_gqa", float("nan"))
+    ms = tm["ms"]
     return {"workload": "chunked-prefill step: 4 x 512-token chunks (prefill call) + 60 decode tokens "
                         "(decode call), contexts log-uniform 4K-142K, 32q/8kv, d128, bf16",
-            "ms": ms, "tokens_per_s": wl.q.shape[0] / (ms * 1e-3), "kernel_ms": kern, "flop": flops,
-            "decode_kv_bytes": kv_bytes,
-            "decode_kv_gbps": kv_bytes / (kern.get("decode_gqa", float("nan")) * 1e-3) / 1e9,
-            "roofline": {"bound": "mfma", "achieved": flops / (k_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": flops / (k_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                         "kernel": "gqa_prefill_kernel"}}
+            "ms": ms, "ms_min": tm["ms_min"], "tokens_per_s": wl.q.shape[0] / (ms * 1e-3), "kernel_ms": _kms(tm),
+            "flop": flops, "decode_kv_bytes": kv_bytes,
+            "decode_kv_gbps": kv_bytes / (_kmean(tm, "decode_gqa") * 1e-3) / 1e9,
+            "roofline": _mfma_roof(flops, _kmean(tm, "prefill_gqa"), "gqa_prefill_kernel",
+                                   "4 x 128 FLOP per (query head, visible key)")}
 
 
 def bench_mla(steps, warmup):
@@ -304,6 +369,7 @@ def bench_mla(steps, warmup):
     t = time.time()
     mla = W.make_mla_decode(4)
     dev = MlaOnDevice(mla)
+    del mla.kv_pool, mla.kv_scale
     log(f"[bench] MLA workload ready in {time.time() - t:.1f}s")
     S, T, H = mla.num_seqs, 4, mla.num_q_heads
     q = dev.q.view(S, T, H, 576)
@@ -315,18 +381,21 @@ def bench_mla(steps, warmup):
         pa.paged_attn_decode(q, dev.pool, dev.bt, dev.total_len, q_per_seq=T, num_q_heads=H,
                              max_context_len=dev.max_total, scale=mla.scale, out=out, workspace=ws)
 
-    ms, kern = timed_steps(step, steps, warmup)
+    tm = timed_steps(step, steps, warmup)
     L = mla.total_len.astype(np.int64)
     pairs = int(sum(4 * l - 6 for l in L))            # sum_j (L - 4 + j + 1), j = 0..3
     flops = pairs * H * 2 * (576 + 512)
     kv_bytes = int(L.sum()) * 580
-    k_ms = kern.get("decode_mla", float("nan"))
+    ms = tm["ms"]
+    k_ms = _kmean(tm, "decode_mla")
+    roof = _mfma_roof(flops, k_ms, "mla_kernel (decode)", "2 x (576 + 512) FLOP per (query row, visible key)")
+    roof["hbm_frac"] = kv_bytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
     return {"workload": "MLA latent decode MTP3: 64 seqs x 4 tokens, 64 heads, FP8 latent 512+64, "
                         "contexts U[32768, 262144], block 64",
-            "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12, "kv_gbps": kv_bytes / (ms * 1e-3) / 1e9,
-            "tokens_per_s": S * T / (ms * 1e-3), "kernel_ms": kern, "flop": flops, "kv_bytes": kv_bytes,
-            "roofline": {"bound": "mfma", "achieved": flops / (k_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": flops / (k_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}}
+            "ms": ms, "ms_min": tm["ms_min"], "tflops": flops / (ms * 1e-3) / 1e12,
+            "kv_gbps": kv_bytes / (ms * 1e-3) / 1e9,
+            "tokens_per_s": S * T / (ms * 1e-3), "kernel_ms": _kms(tm), "flop": flops, "kv_bytes": kv_bytes,
+            "roofline": roof}
 
 
 def bench_sparse(steps, warmup):
@@ -350,21 +419,29 @@ def bench_sparse(steps, warmup):
                             workspace=ws)
         pa.sparse_mla_attn(dev.q, dev.pool, dev.bt, dev.q_seq, topk, scale=mla.scale, out=out)
 
-    ms, kern = timed_steps(step, steps, warmup)
+    tm = timed_steps(step, steps, warmup)
     cached = int(mla.total_len[0] - mla.n_new[0])
     pairs = sum(cached + i + 1 for i in range(n_q))
     idx_flops = pairs * 64 * 128 * 2
     sp_flops = n_q * k * 64 * 2 * (576 + 512)
-    out = {"workload": "indexer (64 heads x 128, FP8 keys) + top-2048 + sparse MLA (64 heads, FP8 latent): "
-                       "1 seq, 131072 cached + 4096 new",
-           "ms": ms, "tokens_per_s": n_q / (ms * 1e-3), "kernel_ms": kern,
-           "indexer_tflops": idx_flops / (kern.get("indexer", float("nan")) * 1e-3) / 1e12,
-           "sparse_mla_tflops": sp_flops / (kern.get("sparse_mla", float("nan")) * 1e-3) / 1e12,
-           "flop": idx_flops + sp_flops}
-    out["roofline"] = {"bound": "mfma", "achieved": out["indexer_tflops"], "peak": BF16_PEAK_TFLOPS,
-                       "unit": "TFLOP/s", "frac": out["indexer_tflops"] / BF16_PEAK_TFLOPS,
-                       "kernel": "indexer_kernel"}
-    return out
+    topk_bytes = pairs * 4 + n_q * k * 4              # the valid scores read once, indices written
+    ms = tm["ms"]
+    k_top = _kmean(tm, "topk")
+    roofs = {
+        "indexer": _mfma_roof(idx_flops, _kmean(tm, "indexer"), "indexer_kernel",
+                              "2 x 128 FLOP per (query, indexer head, visible key)"),
+        "topk": {"bound": "hbm", "achieved": topk_bytes / (k_top * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                 "unit": "GB/s", "frac": topk_bytes / (k_top * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                 "kernel": "topk_kernel", "bytes_per_launch": topk_bytes,
+                 "per_unit": "4 B per valid score (read once) + 4 B per selected index"},
+        "sparse_mla": _mfma_roof(sp_flops, _kmean(tm, "sparse_mla"), "mla_kernel (sparse)",
+                                 "2 x (576 + 512) FLOP per (query row, selected key)"),
+    }
+    return {"workload": "indexer (64 heads x 128, FP8 keys) + top-2048 + sparse MLA (64 heads, FP8 latent): "
+                        "1 seq, 131072 cached + 4096 new",
+            "ms": ms, "ms_min": tm["ms_min"], "tokens_per_s": n_q / (ms * 1e-3), "kernel_ms": _kms(tm),
+            "indexer_tflops": roofs["indexer"]["achieved"], "sparse_mla_tflops": roofs["sparse_mla"]["achieved"],
+            "flop": idx_flops + sp_flops, "roofline": roofs["indexer"], "rooflines": roofs}
 
 
 def bench_append(steps, warmup):
@@ -413,17 +490,34 @@ def bench_append(steps, warmup):
         pa.paged_kv_append(mla5, *d5, x5, max_new_len=4096)
         pa.paged_kv_append(idx5, *d5, xi5, max_new_len=4096)
 
-    ms, kern = timed_steps(step, steps, warmup)
+    tm = timed_steps(step, steps, warmup)
+    ms = tm["ms"]
     gqa_bytes = 2 * (16384 * 8 * 128 * 2 * 2)
     fp8_bytes = 256 * (576 * 3 + 4) + 4096 * (576 * 3 + 4) + 4096 * (128 * 3 + 4)
-    k_ms = kern.get("append_gqa", float("nan"))
+    k_ms = _kmean(tm, "append_gqa")
     ach = gqa_bytes / (k_ms * 1e-3) / 1e9
     return {"workload": "KV append: 8 x 2048 bf16 rows (8 KV heads x 128) + 64 x 4 and 4096 FP8 latent "
                         "rows (576) + 4096 FP8 indexer rows (128), per-token quantisation",
-            "ms": ms, "kernel_ms": kern, "bytes": gqa_bytes + fp8_bytes,
+            "ms": ms, "kernel_ms": _kms(tm), "bytes": gqa_bytes + fp8_bytes,
             "gbps": (gqa_bytes + fp8_bytes) / (ms * 1e-3) / 1e9,
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": ach / HBM_PEAK_GBS, "kernel": "append_gqa_kernel"}}
+
+
+def _clocks():
+    """Current engine / memory clock levels as the driver reports them (best effort)."""
+    out = {}
+    for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+        for card in sorted(os.listdir("/sys/class/drm")) if os.path.isdir("/sys/class/drm") else []:
+            path = f"/sys/class/drm/{card}/device/{name}"
+            try:
+                cur = [l.strip() for l in open(path) if l.strip().endswith("*")]
+            except OSError:
+                continue
+            if cur:
+                out[name[7:]] = cur[0]
+                break
+    return out
 
 
 def main():
@@ -431,19 +525,27 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--secondary", default="", help="comma list of extra workloads: 2n (decode with no "
-                                                    "shared blocks), 3 (prefill), 4 (MLA MTP3 decode), "
-                                                    "5 (indexer + sparse MLA), a (KV append), c (cold-prompt prefill), "
-                                                    "m (chunked-prefill step)")
+    ap.add_argument("--secondary", default="3,4,5",
+                    help="comma list of extra workloads (default 3,4,5; '' for none): 2n (decode with no "
+                         "shared blocks), 3 (suffix prefill), 4 (MLA MTP3 decode), 5 (indexer + top-k + "
+                         "sparse MLA), a (KV append), c (cold-prompt prefill), m (chunked-prefill step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (reference kernel for HBM counters)")
-    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle wall time")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the paged-attention kernels "
                                    "are single-device; multi-GPU context splitting is not built"}))
         sys.exit(2)
+    import workloads as W
+    t = time.time()
+    wl = W.make_gqa_decode(2)
+    log(f"[bench] decode batch generated in {time.time() - t:.1f}s")
+    cpu = None
+    if not args.no_cpu_baseline:       # before the GPU is touched: the workers are plain forks
+        cpu = cpu_baseline(wl, args.cpu_budget)
+        log(f"[bench] cpu baseline: {cpu['sample']}")
     import torch
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
@@ -458,29 +560,33 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    res, wl = bench_decode(args, dev_name)
+    res, wl = bench_decode(args, dev_name, wl=wl)
+    log(f"[bench] decode: {res['ms_per_step']:.4f} ms/step, kernel {res['kernel_ms'].get('decode_gqa', 0):.4f} ms")
     line = {"metric": METRIC, "value": res["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "config": res["config"], "tokens_per_s": res["tokens_per_s"],
-            "unique_kv_gbps": res["unique_kv_gbps"], "kernel_ms": res["kernel_ms"], "roofline": res["roofline"]}
+            "config": res["config"]}
+    for k in ("ms_per_step_min", "ms_per_step_mean", "wall_ms_per_step_incl_flush", "effective_kv_gbps",
+              "tokens_per_s", "kernel_ms", "kernel_ms_median", "workspace_bytes", "roofline"):
+        line[k] = res[k]
+    line["clocks"] = _clocks()
     if args.secondary:
         sec = {}
         for c in [x.strip() for x in args.secondary.split(",") if x.strip()]:
             if c == "2n":   # control: the same decode batch with no shared blocks
                 r, _ = bench_decode(args, dev_name, share=False)
-                sec["decode_no_sharing"] = {k: r[k] for k in ("ms_per_step", "value", "unique_kv_gbps",
+                sec["decode_no_sharing"] = {k: r[k] for k in ("ms_per_step", "value", "effective_kv_gbps",
                                                               "tokens_per_s", "kernel_ms", "roofline")}
                 continue
             f = {"3": ("prefill_suffix", bench_prefill), "4": ("mla_decode_mtp3", bench_mla),
                  "5": ("indexer_topk_sparse_mla", bench_sparse), "a": ("kv_append", bench_append),
                  "c": ("cold_prompt_prefill", bench_cold), "m": ("chunked_prefill_step", bench_chunked)}[c]
-            sec[f[0]] = f[1](max(2, args.steps // 4), max(1, args.warmup // 2))
+            sec[f[0]] = f[1](max(3, args.steps // 4), max(1, args.warmup // 2))
+            log(f"[bench] {f[0]}: {sec[f[0]]['ms']:.3f} ms")
             torch.cuda.empty_cache()
         line["secondary"] = sec
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
-        line["cpu_baseline"]["unit"] = "GB/s"
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

@@ -49,6 +49,19 @@
  *     workspace of at least *_workspace_size(...) bytes (16-byte aligned).
  *   - No C++ exception crosses this interface.  Thread-safe across streams.
  *   - lse outputs (nullable) are natural-log log-sum-exp of the scaled logits, fp32.
+ *   - Value domains.  Inputs must be finite.  Some operands are converted once from bf16
+ *     to fp16 inside the kernels (round toward zero): the prefill's V values and the MLA
+ *     / sparse-MLA queries.  The conversion is exact for magnitudes in [2^-14, 65504];
+ *     smaller ones become fp16 subnormals (absolute error < 2^-25) and larger ones
+ *     saturate to +-65504, so those operands must stay within +-65504.  Softmax
+ *     probabilities are fed to P.V as fp16 (prefill, MLA) or as a bf16 hi + lo pair
+ *     (GQA decode); FP8 values convert to fp16 / bf16 exactly.
+ *   - Library state.  Besides the thread-local error text, the library keeps (a) the
+ *     compute-unit count of each device it has run on (read once per device and process,
+ *     used to size grids and the prefill split), and (b) the optional profiling tables of
+ *     pa_profile_*, which exist only between pa_profile_enable and pa_profile_disable and
+ *     are guarded by a mutex.  Neither holds caller pointers; no call's result depends on
+ *     them except through the device's compute-unit count.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -113,9 +126,12 @@ int32_t pa_version(void);
  *   pool      GQA/MHA bf16 pool; num_q_heads % num_kv_heads == 0; query head h reads
  *             KV head h / (num_q_heads/num_kv_heads).
  *   block_table dev int32 [num_seqs][bt_stride].
- *   cached_len, new_len  dev int32 [num_seqs];  q_start dev int32 [num_seqs+1].
- *   max_new_len    host upper bound of new_len[s] (grid sizing; larger values are
- *                  clamped to it in the kernel).
+ *   cached_len, new_len  dev int32 [num_seqs];  q_start dev int32 [num_seqs+1].  The
+ *             rows q_start[s] .. q_start[s]+min(new_len[s], max_new_len)-1 must lie inside
+ *             q and out; gaps between the sequences' rows are allowed and never touched.
+ *   max_new_len    host upper bound of new_len[s] (grid sizing).  A sequence with more
+ *                  new tokens has only its first max_new_len computed (at positions
+ *                  cached_len[s] + j); the output rows of the rest are not written.
  *   max_total_len  host upper bound of cached_len[s]+new_len[s].
  *   scale     softmax scale (1/sqrt(head_dim) for the pages' workloads).
  *   out       dev bf16 [total_q][num_q_heads][head_dim].
@@ -127,7 +143,9 @@ int32_t pa_version(void);
  * keys of each tile are split into ranges whose partial (output, log-sum-exp) pairs are
  * merged in a fixed order; paged_attn_prefill_workspace_size() then returns the bytes of
  * those partials (0 when the call runs unsplit).  The choice depends only on the sizes
- * and the device, so the size query and the call agree; results are deterministic.
+ * and the device, so the size query and the call agree; results are deterministic.  The
+ * partials of new token j of sequence s live in token slot s * max_new_len + j, so the
+ * call never writes past the workspace size returned for the same num_seqs and maxima.
  * ------------------------------------------------------------------------------- */
 size_t paged_attn_prefill_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                          int32_t max_new_len, int32_t max_total_len,

@@ -10,7 +10,8 @@ operation the passage names:
 Conventions (the pages are silent; these are the plain readings):
   * key t is visible to a query at logical position p iff t <= p (inclusive causal);
   * GQA: query head h reads KV head h // (Hq / Hkv);
-  * softmax is computed exactly in two passes (max, then exp/sum), never online.
+  * softmax is computed exactly in two passes (max, then exp/sum), never online;
+  * the contractions are plain float64 matrix products (numpy matmul, BLAS).
 """
 from __future__ import annotations
 
@@ -86,11 +87,11 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndarray, sc
         for i0 in range(0, n, rows):
             i1 = min(n, i0 + rows)
             qs = q[i0:i1, g * G:(g + 1) * G, :]                     # [r][G][d]
-            s = np.einsum("rgd,td->rgt", qs, kg) * scale            # [r][G][L]
+            s = np.matmul(qs, kg.T) * scale                          # [r][G][L]
             mask = t[None, None, :] > q_pos[i0:i1, None, None]
             s = np.where(mask, -np.inf, s)
             p, l_ = _softmax_rows(s)
-            o[i0:i1, g * G:(g + 1) * G, :] = np.einsum("rgt,te->rge", p, vg)
+            o[i0:i1, g * G:(g + 1) * G, :] = np.matmul(p, vg)
             lse[i0:i1, g * G:(g + 1) * G] = l_
     return o, lse
 
@@ -176,8 +177,8 @@ def indexer_scores(q_bits: np.ndarray, w: np.ndarray, k_codes: np.ndarray, k_sca
     rows = max(1, _ROW_CHUNK_BYTES // (8 * max(1, L) * q.shape[1]))
     for i0 in range(0, n, rows):
         i1 = min(n, i0 + rows)
-        s = np.einsum("ihd,td->iht", q[i0:i1], k)             # [r][H][L]
-        sc = np.einsum("ih,iht->it", wf[i0:i1], np.maximum(s, 0.0))
+        s = np.matmul(q[i0:i1], k.T)                          # [r][H][L]
+        sc = np.matmul(wf[i0:i1, None, :], np.maximum(s, 0.0))[:, 0, :]   # sum over heads
         out[i0:i1] = np.where(t[None, :] > np.asarray(q_pos[i0:i1])[:, None], -np.inf, sc)
     return out
 

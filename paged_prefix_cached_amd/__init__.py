@@ -143,17 +143,19 @@ def indexer_pool(keys, scale) -> KVPool:
 # --------------------------------------------------------------------------- calls
 def paged_attn_prefill(q, pool: KVPool, block_table, cached_len, new_len, q_start, *,
                        num_q_heads: int, max_new_len: int, max_total_len: int, scale: float,
-                       out=None, lse=None):
+                       out=None, lse=None, workspace=None):
     lib = load()
     if out is None:
         out = _bf16_out((q.shape[0], num_q_heads, pool.head_dim_v), q)
-    nws = lib.paged_attn_prefill_workspace_size(block_table.shape[0], num_q_heads, max_new_len,
-                                                max_total_len, ctypes.byref(pool))
-    ws = _ws(nws, q)
+    if workspace is None:
+        nws = lib.paged_attn_prefill_workspace_size(block_table.shape[0], num_q_heads, max_new_len,
+                                                    max_total_len, ctypes.byref(pool))
+        workspace = _ws(nws, q)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.paged_attn_prefill(_p(q), ctypes.byref(pool), _p(block_table), block_table.shape[1],
                                   _p(cached_len), _p(new_len), _p(q_start), block_table.shape[0],
                                   num_q_heads, max_new_len, max_total_len, scale, _p(out), _p(lse),
-                                  _p(ws), nws, _stream(q)), "paged_attn_prefill")
+                                  _p(workspace), nbytes, _stream(q)), "paged_attn_prefill")
     return out
 
 

@@ -542,8 +542,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const int total = min(cached + nl, a.pf_max_total);
     const int vis = min(cached + j, total - 1) + 1;  // keys the token sees
     n = vis > 0 ? min((vis + a.split - 1) / a.split, a.max_splits) : 0;
-    s = a.pf_q_start[seq] + j;
-    base = (size_t)s * a.max_splits * a.rows + row;
+    base = ((size_t)seq * a.pf_max_new + j) * a.max_splits * a.rows + row;   // token slot
+    s = a.pf_q_start[seq] + j;                                                // output row
     stride = a.rows;
   } else if (a.unit_start != nullptr) {
     const int Hq = a.rows / a.q_per_seq, G = Hq / a.num_kv_heads, R = a.q_per_seq * G;

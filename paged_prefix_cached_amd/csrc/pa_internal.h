@@ -51,7 +51,8 @@ struct GqaPrefillArgs {
   float scale_log2;  // softmax scale * log2(e)
   // Split-K (split_len > 0): the keys of a tile are cut into ranges of split_len; each
   // workgroup writes the partial (o, log2-sum-exp) of one range for its rows at
-  // [token][split][num_q_heads] of part_o / part_lse, and the combine kernel merges them.
+  // [seq * max_new_len + token][split][num_q_heads] of part_o / part_lse, and the combine
+  // kernel merges them.
   float* part_o;
   float* part_lse;
   int32_t split_len, max_splits;
@@ -93,7 +94,8 @@ struct CombineArgs {
   const int32_t* unit_start;
   int32_t members, n_chunks, num_kv_heads, q_per_seq;
   // Split-K prefill partials (pf_q_start != null): workgroup (s, j, head) merges the
-  // partials of new token j of sequence s, written at [token][split][rows] (rows = heads).
+  // partials of new token j of sequence s, written at [s * pf_max_new + j][split][rows]
+  // (rows = heads), and writes output row q_start[s] + j.
   const int32_t* pf_q_start;
   const int32_t* pf_cached;
   const int32_t* pf_new_len;

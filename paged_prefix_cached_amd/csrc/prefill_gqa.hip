@@ -286,8 +286,10 @@ __global__ __launch_bounds__(kThreads, 2) void gqa_prefill_kernel(GqaPrefillArgs
   if (!row_ok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (a.split_len > 0) {
-    // partial of this key range: o (normalised over the range) and its log2-sum-exp
-    const size_t slot = ((size_t)(a.q_start[s] + tok_c) * a.max_splits + split) * Hq + g * G + hh;
+    // partial of this key range: o (normalised over the range) and its log2-sum-exp, at
+    // [s * max_new_len + token][split][head] -- indexed by the sequence's own token slot,
+    // never by q_start, so the workspace of num_seqs * max_new_len token slots always holds it
+    const size_t slot = (((size_t)s * a.max_new_len + tok_c) * a.max_splits + split) * Hq + g * G + hh;
     float* po = a.part_o + slot * D;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)

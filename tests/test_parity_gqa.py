@@ -212,3 +212,44 @@ def test_prefill_split_k_long_contexts(pa_lib):
     # fixed-order merge: bit-identical on a rerun
     out2, lse2 = _prefill(pa_lib, dev)
     assert bf16_out(out2).tobytes() == got.tobytes() and np.array_equal(lse2.cpu().numpy(), lg)
+
+
+def test_prefill_split_k_clamped_lengths_and_gapped_rows(pa_lib):
+    """Split-K with a new_len above the host maximum and gaps between the sequences' query
+    rows: only the first max_new_len new tokens of a sequence are computed, rows outside
+    the sequences and past the clamp are never written, and nothing past the caller's
+    workspace of paged_attn_prefill_workspace_size bytes changes."""
+    import torch
+    from workloads.device import t as to_dev
+    wl = W.make_chunked_mixed(10, n_chunked=2, chunk=100, n_decode=3, lo=40000, hi=70000,
+                              num_q_heads=8, num_kv_heads=2, head_dim=128, keep_content=True)
+    dev = GqaOnDevice(wl)
+    S, H, D, max_new = wl.num_seqs, 8, 128, 60
+    gap = 7
+    q_start2 = (wl.q_start + gap * np.arange(S + 1)).astype(np.int32)
+    n_rows = int(q_start2[-1])
+    q2 = np.zeros((n_rows, H, D), np.uint16)
+    for s in range(S):
+        q2[q_start2[s]:q_start2[s] + wl.n_new[s]] = wl.q_rows(s)
+    q2_d, qs2_d = to_dev(q2, "cuda"), to_dev(q_start2, "cuda")
+    nws = pa_lib.load().paged_attn_prefill_workspace_size(S, H, max_new, dev.max_total, pa_lib.ctypes.byref(dev.pool))
+    assert nws > 0                                         # split-K taken
+    guard = 1 << 20
+    ws = torch.full((nws + guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    sentinel = torch.tensor(0x7F80, dtype=torch.int16)     # bf16 +inf bit pattern
+    out = torch.full((n_rows, H, D), 0x7F80, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    pa_lib.paged_attn_prefill(q2_d, dev.pool, dev.bt, dev.cached, dev.n_new, qs2_d, num_q_heads=H,
+                              max_new_len=max_new, max_total_len=dev.max_total, scale=wl.scale, out=out,
+                              workspace=ws[:nws])
+    torch.cuda.synchronize()
+    assert torch.all(ws[nws:] == 0xA5), "a write landed past the workspace"
+    raw = out.view(torch.int16).cpu()
+    got = bf16_out(out)
+    written = np.zeros(n_rows, bool)
+    for s in range(S):
+        n = min(int(wl.n_new[s]), max_new)
+        a = int(q_start2[s])
+        written[a:a + n] = True
+        ro, _ = oracle.paged_gqa_attention(wl, s)
+        assert_close(got[a:a + n], ro[:n], BF16_MAX_ABS, BF16_L1, f"clamped split-K seq={s}")
+    assert torch.all(raw[torch.from_numpy(~written)] == sentinel), "rows outside the computed tokens changed"
