@@ -186,6 +186,31 @@ pa_status paged_attn_decode(const void* q, const pa_kv_pool* pool,
                             hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
+ * 2b. Decode without a workspace argument, for callers that cannot allocate device
+ *     memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ *     hipMalloc.  Same arguments, kernels and results as paged_attn_decode (bit for bit),
+ *     minus the workspace: the call runs on a scratch array of PA_NOALLOC_SCRATCH_BYTES
+ *     that the library keeps in device memory, one per GPU, held until the process ends.
+ *     It allocates nothing and calls no allocating routine.
+ *   Limit: sizes whose paged_attn_decode_workspace_size(...) exceeds
+ *     PA_NOALLOC_SCRATCH_BYTES are rejected with PA_ERR_WORKSPACE before anything is
+ *     launched (use paged_attn_decode with a workspace for those).
+ *   Concurrency: every call on one GPU uses that GPU's one scratch array.  Calls that
+ *     overlap on one GPU (different streams, or different host threads without ordering)
+ *     race on it and give undefined results; calls in one stream are ordered and safe.
+ *     The array keeps the last call's contents; each call writes every part it later
+ *     reads, so nothing needs clearing between calls.
+ * ------------------------------------------------------------------------------- */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+size_t paged_attn_decode_noalloc_max_bytes(void);
+pa_status paged_attn_decode_noalloc(const void* q, const pa_kv_pool* pool,
+                                    const int32_t* block_table, int32_t bt_stride,
+                                    const int32_t* context_len, int32_t num_seqs,
+                                    int32_t q_per_seq, int32_t num_q_heads,
+                                    int32_t max_context_len, float scale, void* out, float* lse,
+                                    hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
  * 3. Indexer scores and top-k ([AgentX] "DeepSeek V4": 64 indexer heads, one global
  *    top-k per token; [GLM] "What's new": 2,048 tokens selected per query token).
  *

@@ -19,7 +19,8 @@ import ctypes
 import os
 
 __all__ = ["load", "PAError", "KVPool", "gqa_pool", "mla_pool", "indexer_pool",
-           "paged_attn_prefill", "paged_attn_decode", "mla_indexer_topk", "sparse_mla_attn",
+           "paged_attn_prefill", "paged_attn_decode", "paged_attn_decode_noalloc", "mla_indexer_topk",
+           "sparse_mla_attn",
            "paged_kv_append", "pa_test_gather_kv", "pa_test_topk_from_scores", "pa_profile_enable",
            "pa_profile_records", "pa_profile_disable", "LIB_PATH"]
 
@@ -50,6 +51,9 @@ _SIGS = {
     "paged_attn_decode_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _vp]),
     "paged_attn_decode": (_c_i32, [_vp, _vp, _vp, _c_i32, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                    _c_f, _vp, _vp, _vp, _c_sz, _vp]),
+    "paged_attn_decode_noalloc_max_bytes": (_c_sz, []),
+    "paged_attn_decode_noalloc": (_c_i32, [_vp, _vp, _vp, _c_i32, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                           _c_f, _vp, _vp, _vp]),
     "mla_indexer_topk_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32]),
     "mla_indexer_topk": (_c_i32, [_vp, _vp, _vp, _vp, _c_i32, _vp, _vp, _vp, _c_i32, _c_i32,
                                   _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _c_sz, _vp]),
@@ -176,6 +180,19 @@ def paged_attn_decode(q, pool: KVPool, block_table, context_len, *, q_per_seq: i
                                  _p(out), _p(lse), _p(workspace),
                                  0 if workspace is None else workspace.numel() * workspace.element_size(),
                                  _stream(q)), "paged_attn_decode")
+    return out
+
+
+def paged_attn_decode_noalloc(q, pool: KVPool, block_table, context_len, *, q_per_seq: int,
+                              num_q_heads: int, max_context_len: int, scale: float, out=None, lse=None):
+    """paged_attn_decode on the library's own per-GPU scratch array (no workspace)."""
+    lib = load()
+    S = block_table.shape[0]
+    if out is None:
+        out = _bf16_out((S, q_per_seq, num_q_heads, pool.head_dim_v), q)
+    _check(lib.paged_attn_decode_noalloc(_p(q), ctypes.byref(pool), _p(block_table), block_table.shape[1],
+                                         _p(context_len), S, q_per_seq, num_q_heads, max_context_len, scale,
+                                         _p(out), _p(lse), _stream(q)), "paged_attn_decode_noalloc")
     return out
 
 

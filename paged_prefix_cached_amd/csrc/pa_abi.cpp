@@ -287,12 +287,11 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t q_per_seq, int
   return decode_layout(num_seqs, q_per_seq, num_q_heads, max_context_len, pool).total();
 }
 
-pa_status paged_attn_decode(const void* q, const pa_kv_pool* pool, const int32_t* block_table,
-                            int32_t bt_stride, const int32_t* context_len, int32_t num_seqs,
-                            int32_t q_per_seq, int32_t num_q_heads, int32_t max_context_len,
-                            float scale, void* out, float* lse, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
-  g_detail[0] = 0;
+static pa_status decode_impl(const void* q, const pa_kv_pool* pool, const int32_t* block_table,
+                             int32_t bt_stride, const int32_t* context_len, int32_t num_seqs,
+                             int32_t q_per_seq, int32_t num_q_heads, int32_t max_context_len,
+                             float scale, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
   PA_TRY(check_decode(pool, num_seqs, q_per_seq, num_q_heads, max_context_len, bt_stride));
   if (q == nullptr || out == nullptr || block_table == nullptr || context_len == nullptr)
     return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
@@ -376,6 +375,66 @@ pa_status paged_attn_decode(const void* q, const pa_kv_pool* pool, const int32_t
   c.split = l.split;
   c.max_context_len = max_context_len;
   return launched(timed("combine", stream, [&] { return pa::launch_combine(c, stream); }), "combine launch");
+}
+
+pa_status paged_attn_decode(const void* q, const pa_kv_pool* pool, const int32_t* block_table,
+                            int32_t bt_stride, const int32_t* context_len, int32_t num_seqs,
+                            int32_t q_per_seq, int32_t num_q_heads, int32_t max_context_len,
+                            float scale, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  g_detail[0] = 0;
+  return decode_impl(q, pool, block_table, bt_stride, context_len, num_seqs, q_per_seq, num_q_heads,
+                     max_context_len, scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+// Decode without a caller workspace: the same kernels run on a fixed scratch array that
+// the library keeps in device memory, one copy per GPU (a __device__ variable exists
+// once in every device's copy of the code object).  The host-side name `scratch` is not a
+// device address; the address of the current device's copy comes from
+// hipGetSymbolAddress, looked up once per device (with that device current) and kept.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+static pa_status device_scratch(void** ptr) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_UNSUPPORTED, "device %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t g = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (g != hipSuccess || p == nullptr)
+      return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(g));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+size_t paged_attn_decode_noalloc_max_bytes(void) { return PA_NOALLOC_SCRATCH_BYTES; }
+
+pa_status paged_attn_decode_noalloc(const void* q, const pa_kv_pool* pool, const int32_t* block_table,
+                                    int32_t bt_stride, const int32_t* context_len, int32_t num_seqs,
+                                    int32_t q_per_seq, int32_t num_q_heads, int32_t max_context_len,
+                                    float scale, void* out, float* lse, hipStream_t stream) {
+  g_detail[0] = 0;
+  PA_TRY(check_decode(pool, num_seqs, q_per_seq, num_q_heads, max_context_len, bt_stride));
+  const size_t need = decode_layout(num_seqs, q_per_seq, num_q_heads, max_context_len, pool).total();
+  if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES)
+    return fail(PA_ERR_WORKSPACE,
+                "paged_attn_decode_noalloc: these sizes need %zu bytes of scratch, more than the %zu the "
+                "library holds; use paged_attn_decode with a caller workspace",
+                need, (size_t)PA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  PA_TRY(device_scratch(&ws));
+  return decode_impl(q, pool, block_table, bt_stride, context_len, num_seqs, q_per_seq, num_q_heads,
+                     max_context_len, scale, out, lse, ws, (size_t)PA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // ------------------------------------------------------------------------- indexer + top-k

@@ -129,3 +129,20 @@ def test_fp8_pool_rows_fit_int32(lib):
     ok = pa.KVPool(2**31 // 64 - 1, 64, 1, 576, 512, 2, FAKE, None, FAKE)
     assert lib.sparse_mla_attn(FAKE, ctypes.byref(ok), FAKE, 10, FAKE, FAKE, 0, 2048, 64, 0.04, FAKE, None,
                                None, 0, None) == 0
+
+
+def test_decode_noalloc_rejects_oversized_calls_before_launch(lib):
+    """The allocation-free decode checks its scratch need on the host: sizes whose
+    workspace exceeds PA_NOALLOC_SCRATCH_BYTES fail with PA_ERR_WORKSPACE before any HIP
+    call (fake device pointers are never touched)."""
+    pool = _gqa_pool(head_dim_qk=128, head_dim_v=128)
+    big = 4_000_000
+    need = lib.paged_attn_decode_workspace_size(64, 1, 32, big, ctypes.byref(pool))
+    assert need > lib.paged_attn_decode_noalloc_max_bytes() == 64 << 20
+    st = lib.paged_attn_decode_noalloc(FAKE, ctypes.byref(pool), FAKE, big // 16, FAKE, 64, 1, 32, big, 0.088,
+                                       FAKE, None, None)
+    assert st == 3, lib.pa_last_error_detail()
+    assert b"scratch" in lib.pa_last_error_detail()
+    # invalid shapes are still reported as such, not as a scratch shortage
+    assert lib.paged_attn_decode_noalloc(FAKE, ctypes.byref(pool), FAKE, 16, FAKE, 1, 5, 32, 256, 0.088, FAKE,
+                                         None, None) == 2
