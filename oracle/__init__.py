@@ -17,14 +17,20 @@ brute-force loops with math.fsum, closed forms, invariants, permuted block table
 special cases (k >= context => dense; GQA == MHA with repeated KV), the OCP E4M3 table.
 The KV append (append.py) quantises each new token to FP8 by a nearest-value search over
 the E4M3 table; that encoder is pinned to the format's halfway points and saturation, to
-the round trip of every code and to PyTorch's own float8_e4m3fn conversion.
+the round trip of every code and to PyTorch's own float8_e4m3fn conversion.  The MXFP4
+indexer keys of the packed per-block layout (E2M1 elements, E8M0 group scales) are decoded
+by table and quantised by a nearest-value search; both are pinned to the OCP MX format's
+values, halfway points, saturation and shared-exponent rule.
 No function here is "parity unpinned".
 """
-from .formats import bf16_to_f64, e4m3_decode  # noqa: F401
+from .formats import bf16_to_f64, e4m3_decode, e2m1_decode, e8m0_decode, mxfp4_decode  # noqa: F401
 from .attention import (  # noqa: F401
     gather_paged, attention, attention_probs, lse_merge, paged_gqa_attention,
-    mla_dequant, mla_attention, indexer_scores, topk_indices, sparse_mla_attention,
+    mla_dequant, mla_attention, indexer_scores, indexer_scores_mxfp4, indexer_scores_from_keys,
+    topk_indices, sparse_mla_attention,
 )
 from .append import (  # noqa: F401
     e4m3_nearest, quantize_token_fp8, token_positions, append_gqa, append_fp8,
+    e2m1_nearest, mx_shared_exponent, quantize_token_mxfp4, packed_fields, append_packed,
+    PACKED_BLOCK_BYTES, PACKED_LATENT, PACKED_LATENT_SCALE, PACKED_KEYS, PACKED_KEY_SCALES,
 )

@@ -17,7 +17,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import bf16_to_f64, e4m3_decode
+from .formats import bf16_to_f64, e4m3_decode, mxfp4_decode
 
 _ROW_CHUNK_BYTES = 1 << 28     # bound the size of one score matrix (rows x keys x 8 B)
 
@@ -168,8 +168,21 @@ def indexer_scores(q_bits: np.ndarray, w: np.ndarray, k_codes: np.ndarray, k_sca
     in the prompt.  k_t = scale_t * e4m3(k_codes_t) is one 128-wide key per token shared
     by every indexer head.  q_bits [n][H][d] bf16, w [n][H] fp32.
     """
+    return indexer_scores_from_keys(q_bits, w, mla_dequant(k_codes, k_scale), q_pos)
+
+
+def indexer_scores_mxfp4(q_bits: np.ndarray, w: np.ndarray, k_packed: np.ndarray, k_scales: np.ndarray,
+                         q_pos: np.ndarray) -> np.ndarray:
+    """indexer_scores with MXFP4 keys ([AgentX] "Hybrid KV cache management": the FP4
+    indexer): k_t = the decoded MXFP4 vector of token t (k_packed [L][d/2] bytes, k_scales
+    [L][d/32] E8M0 codes)."""
+    return indexer_scores_from_keys(q_bits, w, mxfp4_decode(k_packed, k_scales), q_pos)
+
+
+def indexer_scores_from_keys(q_bits: np.ndarray, w: np.ndarray, k: np.ndarray, q_pos: np.ndarray) -> np.ndarray:
+    """I[i, t] = sum_h w[i,h] * max(0, <q[i,h], k[t]>) for t <= pos(i), else -inf, with the
+    keys already decoded to float64 k [L][d]."""
     q = bf16_to_f64(q_bits)                                   # [n][H][d]
-    k = mla_dequant(k_codes, k_scale)                         # [L][d]
     wf = np.asarray(w, dtype=np.float64)
     n, L = q.shape[0], k.shape[0]
     out = np.empty((n, L), dtype=np.float64)

@@ -10,7 +10,7 @@ never reconstructed.
 Everything here is storage-format plumbing: random draws, bf16 / FP8-E4M3 rounding,
 block pools, block tables.  No attention, score or top-k arithmetic lives here.
 
-Layouts (all row-major, int32 indices):
+Layouts (all row-major, int32 indices; the packed per-block layout is at pack_mla_blocks):
   GQA pool   k_pool, v_pool : bf16 bits  uint16 [num_blocks][Hkv][16][d]
   MLA pool   kv_pool        : e4m3 bytes uint8  [num_blocks][64][576]  (0..511 latent = V)
              kv_scale       : float32           [num_blocks][64]
@@ -32,7 +32,8 @@ __all__ = [
     "fp8_quantize_tokens", "normal_f32", "PagedGQA", "PagedMLA", "IndexerInput",
     "make_prefill_tiny", "make_gqa_decode", "make_prefix_prefill", "make_mla_decode",
     "make_sparse_mla", "make_gqa", "tie_scores", "CONFIG_NAMES", "AppendInput", "make_append",
-    "make_cold_prefill", "make_chunked_mixed",
+    "make_cold_prefill", "make_chunked_mixed", "mxfp4_quantize_tokens", "pack_mla_blocks",
+    "PACKED_BLOCK_BYTES",
 ]
 
 BF16_NAN = np.uint16(0x7FC0)
@@ -99,6 +100,26 @@ def fp8_quantize_tokens(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
     codes = e4m3_encode(x / scale[..., None])
     return codes, scale
+
+
+def mxfp4_quantize_tokens(x: np.ndarray, group: int = 32) -> tuple[np.ndarray, np.ndarray]:
+    """MXFP4 storage of x[..., D]: per group of 32, E8M0 code e = floor(log2 amax) - 2 + 127
+    (127 for an all-zero group, kept in [2, 252]), elements E2M1 of x / 2^(e-127) rounded to
+    nearest, ties to even, saturating at 6; two elements a byte, element 2j in the low
+    nibble.  Returns (packed [..., D/2] uint8, scale codes [..., D/32] uint8)."""
+    x = np.asarray(x, dtype=np.float32)
+    lead = x.shape[:-1]
+    g = x.reshape(lead + (x.shape[-1] // group, group)).astype(np.float64)
+    amax = np.max(np.abs(g), axis=-1)
+    _, p = np.frexp(amax)
+    e = np.where(amax > 0, np.clip(p - 1 - 2 + 127, 2, 252), 127).astype(np.int64)
+    y = g / np.ldexp(1.0, e - 127)[..., None]
+    a = np.abs(y)
+    mag = ((a > 0.25).astype(np.uint8) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5) + (a >= 3.5)
+           + (a > 5.0)).astype(np.uint8)
+    code = (mag | np.where(np.signbit(y), np.uint8(8), np.uint8(0))).reshape(x.shape)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    return packed, e.astype(np.uint8)
 
 
 def normal_f32(seed: int, stream: int, n: int, *, chunk: int = 1 << 22) -> np.ndarray:
@@ -427,6 +448,27 @@ def _fp8_tokens(seed: int, stream: int, n_tokens: int, dim: int, *, chunk_tokens
     return codes, scales
 
 
+def _mxfp4_tokens(seed: int, stream: int, n_tokens: int, dim: int, *, chunk_tokens: int = 1 << 15):
+    """n_tokens N(0,1) vectors of width dim (the same draws as _fp8_tokens for the same
+    seed and stream), stored as MXFP4."""
+    packed = np.empty((n_tokens, dim // 2), dtype=np.uint8)
+    scales = np.empty((n_tokens, dim // 32), dtype=np.uint8)
+    nchunks = max(1, -(-n_tokens // chunk_tokens))
+
+    def fill(c: int) -> None:
+        lo, hi = c * chunk_tokens, min(n_tokens, (c + 1) * chunk_tokens)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(stream, c))))
+        x = g.standard_normal((hi - lo, dim), dtype=np.float32)
+        packed[lo:hi], scales[lo:hi] = mxfp4_quantize_tokens(x)
+
+    if nchunks == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return packed, scales
+
+
 def _paged_fp8(seed: int, stream: int, lengths, dim: int, bs: int, perm_stream: int,
                keep_content: bool):
     """Private (unshared) FP8 token pool for the given sequence lengths."""
@@ -486,6 +528,9 @@ class IndexerInput:
     w: np.ndarray                  # float32 [n_q][H_idx]
     content_k: np.ndarray | None = None     # uint8 [n_unique][bs][128]
     content_scale: np.ndarray | None = None
+    # MXFP4 keys of the packed layout (make_sparse_mla(..., fp4_keys=True)): the same draws
+    fp4_pool: np.ndarray | None = None       # uint8 [NB][bs][64]  (two E2M1 a byte)
+    fp4_scale: np.ndarray | None = None      # uint8 [NB][bs][4]   (E8M0 per 32 elements)
 
     def k_contiguous(self, mla: PagedMLA, s: int) -> tuple[np.ndarray, np.ndarray]:
         assert self.content_k is not None
@@ -497,9 +542,11 @@ class IndexerInput:
 
 def make_sparse_mla(seed: int = 5, *, cached: int = 131072, new: int = 4096, num_q_heads: int = 64,
                     idx_heads: int = 64, idx_dim: int = 128, q_mult: float = 1.0,
-                    keep_content: bool = False, lengths=None, n_new=None):
+                    keep_content: bool = False, lengths=None, n_new=None, fp4_keys: bool = False):
     """One (or more) sequences with `cached` prefix tokens and `new` query tokens.
-    Returns (PagedMLA for the latent cache and MLA queries, IndexerInput)."""
+    Returns (PagedMLA for the latent cache and MLA queries, IndexerInput).  With fp4_keys
+    the indexer keys are also stored as MXFP4 (fp4_pool / fp4_scale, same draws, same
+    block table) for the packed per-block layout."""
     if lengths is None:
         lengths = np.array([cached + new], dtype=np.int64)
         n_new = np.array([new], dtype=np.int64)
@@ -525,6 +572,21 @@ def make_sparse_mla(seed: int = 5, *, cached: int = 131072, new: int = 4096, num
         phys = bt[s, :nb[s]].astype(np.int64)
         ipool[phys] = kc[logical[s]]
         iscale[phys] = ks[logical[s]]
+    fpool = fscale = None
+    if fp4_keys:
+        fk, fs = _mxfp4_tokens(seed, 7, n_unique * MLA_BLOCK, idx_dim)
+        fk = fk.reshape(n_unique, MLA_BLOCK, idx_dim // 2)
+        fs = fs.reshape(n_unique, MLA_BLOCK, idx_dim // 32)
+        fpool = np.full((NB, MLA_BLOCK, idx_dim // 2), 0x77, dtype=np.uint8)     # poison: NaN scales
+        fscale = np.full((NB, MLA_BLOCK, idx_dim // 32), 0xFF, dtype=np.uint8)
+        for s in range(S):
+            tail = int(nb[s] * MLA_BLOCK - lengths[s])
+            if tail:     # large finite garbage in the unused tail: 6 * 2^73
+                fk[logical[s][-1], MLA_BLOCK - tail:, :] = np.uint8(0x77)
+                fs[logical[s][-1], MLA_BLOCK - tail:, :] = np.uint8(200)
+            phys = bt[s, :nb[s]].astype(np.int64)
+            fpool[phys] = fk[logical[s]]
+            fscale[phys] = fs[logical[s]]
     q_start = np.zeros(S + 1, dtype=np.int32)
     q_start[1:] = np.cumsum(n_new)
     nq = int(q_start[-1])
@@ -535,8 +597,27 @@ def make_sparse_mla(seed: int = 5, *, cached: int = 131072, new: int = 4096, num
                    n_new.astype(np.int32), q_start, bt, pool, pscale, q, logical, ck, cs,
                    CONFIG_NAMES[5])
     idx = IndexerInput(ipool, iscale, q_idx, w, kc if keep_content else None,
-                       ks if keep_content else None)
+                       ks if keep_content else None, fpool, fscale)
     return mla, idx
+
+
+# --------------------------------------------------------------------------- packed blocks
+# One allocation per 64-token block for every cache group of the MLA layer: bytes
+# [0, 36864) FP8 latent [64][576]; [36864, 37120) fp32 latent scales [64]; [37120, 41216)
+# MXFP4 index keys [64][64]; [41216, 41472) E8M0 key scales [64][4].
+PACKED_BLOCK_BYTES = 41472
+
+
+def pack_mla_blocks(mla: PagedMLA, idx: IndexerInput) -> np.ndarray:
+    """The packed pool [NB][41472] bytes of a latent pool plus its MXFP4 index keys (same
+    block ids).  Byte copies only."""
+    nb = mla.kv_pool.shape[0]
+    out = np.empty((nb, PACKED_BLOCK_BYTES), dtype=np.uint8)
+    out[:, :36864] = mla.kv_pool.reshape(nb, -1)
+    out[:, 36864:37120] = np.ascontiguousarray(mla.kv_scale, dtype=np.float32).view(np.uint8).reshape(nb, -1)
+    out[:, 37120:41216] = idx.fp4_pool.reshape(nb, -1)
+    out[:, 41216:] = idx.fp4_scale.reshape(nb, -1)
+    return out
 
 
 # --------------------------------------------------------------------------- top-k fixtures
