@@ -21,7 +21,8 @@ sequence's whole context instead (shared prefix blocks once per sequence).  The 
 object uses the same algorithmic bytes over the decode kernel's average launch time.
 `cpu_baseline` times the CPU oracle (oracle/) on the same batch with a process pool over
 the sequences, one single-threaded process per host core.  `secondary` holds the other
-workloads (suffix prefill, MLA MTP3 decode, indexer + top-k + sparse MLA by default).
+workloads (suffix prefill, MLA MTP3 decode, indexer + top-k + sparse MLA on separate pools
+and on the packed per-block layout with MXFP4 index keys, by default).
 """
 from __future__ import annotations
 
@@ -398,14 +399,21 @@ def bench_mla(steps, warmup):
             "roofline": roof}
 
 
-def bench_sparse(steps, warmup):
+def bench_sparse(steps, warmup, packed=False):
+    """Indexer + top-2,048 + sparse MLA at 131,072 + 4,096 tokens.  packed: the packed
+    per-block layout (one allocation per 64-token block: FP8 latent + scales + MXFP4 index
+    keys + E8M0 scales), the indexer reading the MXFP4 keys and sparse MLA the latent view."""
     import torch
     import paged_prefix_cached_amd as pa
     import workloads as W
-    from workloads.device import MlaOnDevice
+    from workloads.device import MlaOnDevice, t as to_dev
     t = time.time()
-    mla, idx = W.make_sparse_mla(5)
+    mla, idx = W.make_sparse_mla(5, fp4_keys=packed)
     dev = MlaOnDevice(mla, idx)
+    lat_pool, idx_pool = dev.pool, dev.idx_pool
+    if packed:
+        blocks = to_dev(W.pack_mla_blocks(mla, idx), "cuda")
+        lat_pool, idx_pool = pa.packed_mla_pools(blocks)
     log(f"[bench] sparse workload ready in {time.time() - t:.1f}s")
     n_q, k = dev.q_idx.shape[0], 2048
     topk = torch.empty((n_q, k), dtype=torch.int32, device="cuda")
@@ -414,10 +422,10 @@ def bench_sparse(steps, warmup):
     out = torch.empty((n_q, 64, 512), dtype=torch.bfloat16, device="cuda")
 
     def step():
-        pa.mla_indexer_topk(dev.q_idx, dev.w, dev.idx_pool, dev.bt, dev.cached, dev.n_new, dev.q_start,
+        pa.mla_indexer_topk(dev.q_idx, dev.w, idx_pool, dev.bt, dev.cached, dev.n_new, dev.q_start,
                             max_new_len=dev.max_new, max_total_len=dev.max_total, k=k, topk_idx=topk,
                             workspace=ws)
-        pa.sparse_mla_attn(dev.q, dev.pool, dev.bt, dev.q_seq, topk, scale=mla.scale, out=out)
+        pa.sparse_mla_attn(dev.q, lat_pool, dev.bt, dev.q_seq, topk, scale=mla.scale, out=out)
 
     tm = timed_steps(step, steps, warmup)
     cached = int(mla.total_len[0] - mla.n_new[0])
@@ -437,8 +445,12 @@ def bench_sparse(steps, warmup):
         "sparse_mla": _mfma_roof(sp_flops, _kmean(tm, "sparse_mla"), "mla_kernel (sparse)",
                                  "2 x (576 + 512) FLOP per (query row, selected key)"),
     }
-    return {"workload": "indexer (64 heads x 128, FP8 keys) + top-2048 + sparse MLA (64 heads, FP8 latent): "
-                        "1 seq, 131072 cached + 4096 new",
+    L = int(mla.total_len[0])
+    kv_per_token = 576 + 4 + (64 + 4 if packed else 128 + 4)
+    return {"workload": ("packed per-block layout: MXFP4 indexer keys" if packed else "indexer (FP8 keys)")
+                        + " (64 heads x 128) + top-2048 + sparse MLA (64 heads, FP8 latent): 1 seq, "
+                        "131072 cached + 4096 new",
+            "kv_bytes_per_token": kv_per_token, "kv_bytes": kv_per_token * L,
             "ms": ms, "ms_min": tm["ms_min"], "tokens_per_s": n_q / (ms * 1e-3), "kernel_ms": _kms(tm),
             "indexer_tflops": roofs["indexer"]["achieved"], "sparse_mla_tflops": roofs["sparse_mla"]["achieved"],
             "flop": idx_flops + sp_flops, "roofline": roofs["indexer"], "rooflines": roofs}
@@ -525,10 +537,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--secondary", default="3,4,5",
-                    help="comma list of extra workloads (default 3,4,5; '' for none): 2n (decode with no "
+    ap.add_argument("--secondary", default="3,4,5,5p",
+                    help="comma list of extra workloads (default 3,4,5,5p; '' for none): 2n (decode with no "
                          "shared blocks), 3 (suffix prefill), 4 (MLA MTP3 decode), 5 (indexer + top-k + "
-                         "sparse MLA), a (KV append), c (cold-prompt prefill), m (chunked-prefill step)")
+                         "sparse MLA), 5p (the same on the packed layout with MXFP4 index keys), a (KV append), "
+                         "c (cold-prompt prefill), m (chunked-prefill step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (reference kernel for HBM counters)")
@@ -579,7 +592,9 @@ def main():
                                                               "tokens_per_s", "kernel_ms", "roofline")}
                 continue
             f = {"3": ("prefill_suffix", bench_prefill), "4": ("mla_decode_mtp3", bench_mla),
-                 "5": ("indexer_topk_sparse_mla", bench_sparse), "a": ("kv_append", bench_append),
+                 "5": ("indexer_topk_sparse_mla", bench_sparse),
+                 "5p": ("packed_fp4_indexer_topk_sparse_mla", lambda st, wu: bench_sparse(st, wu, packed=True)),
+                 "a": ("kv_append", bench_append),
                  "c": ("cold_prompt_prefill", bench_cold), "m": ("chunked_prefill_step", bench_chunked)}[c]
             sec[f[0]] = f[1](max(3, args.steps // 4), max(1, args.warmup // 2))
             log(f"[bench] {f[0]}: {sec[f[0]]['ms']:.3f} ms")

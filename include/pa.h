@@ -83,6 +83,7 @@ typedef int pa_status;
 
 #define PA_BF16 1
 #define PA_FP8_E4M3 2
+#define PA_PACKED_MLA 3
 
 /* One shared block pool ([AgentX] "Hybrid KV cache management").
  *   GQA / MHA (kv_dtype PA_BF16, block_size 16, head_dim_qk == head_dim_v in {64, 128}):
@@ -96,7 +97,25 @@ typedef int pa_status;
  *   Indexer keys (kv_dtype PA_FP8_E4M3, block_size 64, num_kv_heads 1,
  *                 head_dim_qk 128, head_dim_v 0): k e4m3 [num_blocks][64][128] plus
  *     scale as above; they share the MLA block table.
- *   FP8 pools: num_blocks * 64 must fit in int32 (PA_ERR_UNSUPPORTED otherwise). */
+ *   Packed per-block layout (kv_dtype PA_PACKED_MLA; [AgentX] "Hybrid KV cache
+ *     management", Figure 5: every cache group of a block in one allocation; with the FP4
+ *     indexer it saves about 10 % of KV memory).  k points to [num_blocks][41472] bytes, v
+ *     and scale are unused (NULL).  A 64-token block holds, at byte offsets:
+ *         0      FP8 E4M3 latent   [64][576]   (as the MLA pool above)
+ *         36864  fp32 latent scale [64]
+ *         37120  MXFP4 index keys  [64][64]    128 FP4 E2M1 elements a token, element 2j
+ *                                              in the low nibble of byte j
+ *         41216  E8M0 key scales   [64][4]     one per 32 elements: 2^(code - 127)
+ *     648 B per token against 712 B for the FP8 latent and FP8 index-key pools.  The MX
+ *     format (OCP Microscaling MXFP4) is the reading of the page's "FP4 indexer"; key
+ *     scale codes must lie in [2, 252] (every decoded element is then a normal bfloat16;
+ *     paged_kv_append only writes such codes).  The same k pointer serves two views:
+ *       latent view   (block_size 64, num_kv_heads 1, head_dim_qk 576, head_dim_v 512)
+ *                     for paged_attn_decode, sparse_mla_attn and the latent append;
+ *       index view    (block_size 64, num_kv_heads 1, head_dim_qk 128, head_dim_v 0)
+ *                     for mla_indexer_topk and the key append (MXFP4 quantisation).
+ *   FP8 and packed pools: num_blocks * 64 must fit in int32 (PA_ERR_UNSUPPORTED
+ *   otherwise). */
 typedef struct {
   int32_t num_blocks;
   int32_t block_size;
@@ -222,7 +241,8 @@ pa_status paged_attn_decode_noalloc(const void* q, const pa_kv_pool* pool,
  * broken toward the lower t, in ascending t, padded with -1 when pos(i)+1 < k.
  *   q_idx     dev bf16 [n_q][num_idx_heads][128]
  *   w         dev fp32 [n_q][num_idx_heads]
- *   idx_pool  FP8 indexer-key pool (see pa_kv_pool)
+ *   idx_pool  FP8 indexer-key pool, or the index view of a packed pool (MXFP4 keys:
+ *             k_t is then the decoded MXFP4 vector, no per-token scale)
  *   topk_idx  dev int32 [n_q][k]
  *   scores_out dev fp32 [n_q][max_total_len] or NULL: row i gets I[i,0..pos(i)] and -inf
  *              after it (-0.0 is written as +0.0).  The top-k is exactly the selection
@@ -280,6 +300,12 @@ pa_status sparse_mla_attn(const void* q, const pa_kv_pool* pool, const int32_t* 
  *           code[e] = OCP E4M3 round-to-nearest-even of x[e]/scale, both divisions IEEE
  *           float32, magnitudes past 448 clamped to 448; pool->scale gets the scale.
  *           The pages print no quantiser: this per-token amax scaling is the plain one.
+ *           Packed pools: the latent view takes [n_tokens][576] rows as above (codes and
+ *           scale into the block's latent fields); the index view takes [n_tokens][128]
+ *           rows quantised to MXFP4 per group of 32 (OCP MX conversion): scale code
+ *           e = floor(log2 amax) - 2 + 127 kept in [2, 252] (127 for an all-zero group),
+ *           element code = E2M1 round-to-nearest-even of x / 2^(e-127), saturating at 6,
+ *           the sign kept (-0 for a negative value that rounds to zero).
  *           pool->k, pool->v and pool->scale must point to writable device memory.
  *   block_table dev int32 [num_seqs][bt_stride]; cached_len, new_len, q_start dev int32
  *           [num_seqs].
@@ -305,7 +331,8 @@ pa_status paged_kv_append(const pa_kv_pool* pool, const int32_t* block_table, in
  *   the pool into contiguous buffers with the same block-table walk the attention
  *   kernels use.  GQA: k_out, v_out dev bf16 [n_tokens][num_kv_heads][head_dim].  FP8
  *   pools: k_out dev bytes [n_tokens][head_dim_qk], scale_out dev fp32 [n_tokens],
- *   v_out unused.  Bit-exact copy.
+ *   v_out unused.  The index view of a packed pool: k_out [n_tokens][64] (FP4 codes),
+ *   scale_out receives each token's 4 E8M0 codes as one 32-bit word.  Bit-exact copy.
  * pa_test_topk_from_scores: the top-k selection stage alone, on caller-given fp32
  *   scores [n_rows][row_stride] with valid_len dev int32 [n_rows]; same ordering and
  *   tie rules as mla_indexer_topk.  Workspace: pa_test_topk_workspace_size.

@@ -9,7 +9,8 @@ Functions (same names as the C entry points):
     paged_attn_prefill, paged_attn_decode, mla_indexer_topk, sparse_mla_attn,
     paged_kv_append
 Pool descriptors:
-    gqa_pool(k_pool, v_pool), mla_pool(kv_pool, kv_scale), indexer_pool(keys, scale)
+    gqa_pool(k_pool, v_pool), mla_pool(kv_pool, kv_scale), indexer_pool(keys, scale),
+    packed_mla_pools(blocks) (latent and index views of the packed per-block layout)
 Test hooks:
     pa_test_gather_kv, pa_test_topk_from_scores
 """
@@ -18,14 +19,14 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["load", "PAError", "KVPool", "gqa_pool", "mla_pool", "indexer_pool",
+__all__ = ["load", "PAError", "KVPool", "gqa_pool", "mla_pool", "indexer_pool", "packed_mla_pools",
            "paged_attn_prefill", "paged_attn_decode", "paged_attn_decode_noalloc", "mla_indexer_topk",
            "sparse_mla_attn",
            "paged_kv_append", "pa_test_gather_kv", "pa_test_topk_from_scores", "pa_profile_enable",
            "pa_profile_records", "pa_profile_disable", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
-PA_BF16, PA_FP8_E4M3 = 1, 2
+PA_BF16, PA_FP8_E4M3, PA_PACKED_MLA = 1, 2, 3
 _lib = None
 
 _c_i32, _c_sz, _vp, _c_f = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -142,6 +143,17 @@ def indexer_pool(keys, scale) -> KVPool:
     pool = KVPool(nb, bs, 1, d, 0, PA_FP8_E4M3, keys.data_ptr(), None, scale.data_ptr())
     pool._keep = (keys, scale)
     return pool
+
+
+def packed_mla_pools(blocks):
+    """The two views of a packed per-block pool [num_blocks][41472] (uint8): (latent view
+    for decode / sparse MLA / latent append, index view for the indexer / key append)."""
+    nb, nbytes = blocks.shape
+    assert blocks.element_size() == 1 and nbytes == 41472
+    lat = KVPool(nb, 64, 1, 576, 512, PA_PACKED_MLA, blocks.data_ptr(), None, None)
+    idx = KVPool(nb, 64, 1, 128, 0, PA_PACKED_MLA, blocks.data_ptr(), None, None)
+    lat._keep = idx._keep = (blocks,)
+    return lat, idx
 
 
 # --------------------------------------------------------------------------- calls

@@ -8,6 +8,8 @@
 // "What's new" (one latent KV row per token) -- the cache holds FP8.  The pages give no
 // quantiser; the one here is per token: scale = amax / 448 (1 when the row is all zero),
 // code = E4M3 round-to-nearest-even of x / scale in IEEE float32, clamped to +-448.
+// The packed per-block layout ("Hybrid KV cache management", Figure 5) keeps the index
+// keys as MXFP4 (the FP4 indexer): see append_mxfp4_kernel.
 //
 // Both kernels are grids of (token range, sequence); a sequence's rows are q_start[s] ..
 // q_start[s] + new_len[s] - 1 of the packed input and go to logical positions
@@ -126,7 +128,8 @@ __global__ __launch_bounds__(64 * kFp8WavesPerBlock) void append_fp8_kernel(Appe
   // IEEE float32 division (correctly rounded): the code of every element is decided on
   // exactly the value x / scale.
   const float scale = amax > 0.f ? amax / 448.f : 1.f;
-  uint8_t* dst = a.fp8_out + slot * D;
+  const long blk = slot >> 6, r = slot & 63;
+  uint8_t* dst = a.fp8_out + blk * a.blk_bytes + r * D;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int c = lane + 64 * i;
@@ -146,7 +149,51 @@ __global__ __launch_bounds__(64 * kFp8WavesPerBlock) void append_fp8_kernel(Appe
     o.y = packed[1];
     *reinterpret_cast<u32x2*>(dst + 8 * c) = o;
   }
-  if (lane == 0) a.scale_out[slot] = scale;
+  if (lane == 0) *reinterpret_cast<float*>(a.scale_out + blk * a.sblk_bytes + 4 * r) = scale;
+}
+
+// MXFP4 rows (the index keys of the packed per-block layout), D = 128: one wave per token,
+// lane l holds elements 2l and 2l + 1, so a group of 32 elements is 16 lanes.  Per group
+// (OCP MX conversion): E8M0 code e = floor(log2 amax) - 2 + 127 -- the exponent field of
+// amax minus 2 -- kept in [2, 252], 127 for an all-zero group; every element is scaled by
+// 2^(127 - e) (exact) and rounded to the nearest E2M1 value, ties to the even code, with
+// saturation at 6: the magnitude code is the number of rounding boundaries below |y|
+// (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5; a tie at a boundary goes to the even side).
+// Element 2j goes to the low nibble of byte j; the four scale codes follow the row.
+__global__ __launch_bounds__(64 * kFp8WavesPerBlock) void append_mxfp4_kernel(AppendArgs a) {
+  constexpr int D = 128;
+  const int s = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * kFp8WavesPerBlock + (threadIdx.x >> 6);
+  const SeqAppend sq = seq_append(a, s);
+  int row;
+  const long slot = dest_slot<64>(a, sq, j, bt_entry(a, s, (sq.c0 + j) >> 6), &row);
+  if (slot < 0) return;                              // the whole wave agrees
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(a.k_new + (size_t)row * D + 2 * lane);
+  const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xffff0000u);
+  float amax = fmaxf(fabsf(x0), fabsf(x1));
+  amax = wave_max_xor(amax, 16);                     // the lane's group of 16 lanes
+  const int field = (int)(__float_as_uint(amax) >> 23);
+  const uint32_t e = amax > 0.f ? (uint32_t)min(max(field - 2, 2), 252) : 127u;
+  const float inv = __uint_as_float((254u - e) << 23);   // 2^(127 - e)
+  auto code = [&](float x) -> uint32_t {
+    const float y = x * inv;
+    const float m = fabsf(y);
+    const uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
+                       (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
+                       (uint32_t)(m > 5.0f);
+    return c | ((__float_as_uint(y) >> 28) & 8u);     // the sign bit
+  };
+  const uint32_t byte = code(x0) | (code(x1) << 4);
+  // four lanes' bytes -> one 32-bit store
+  const uint32_t b1 = __shfl_down(byte, 1), b2 = __shfl_down(byte, 2), b3 = __shfl_down(byte, 3);
+  const long blk = slot >> 6, r = slot & 63;
+  uint8_t* dst = a.fp8_out + blk * a.blk_bytes + r * (D / 2);
+  if ((lane & 3) == 0)
+    *reinterpret_cast<uint32_t*>(dst + lane) = byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
+  const uint32_t e1 = __shfl(e, 16), e2 = __shfl(e, 32), e3 = __shfl(e, 48);
+  if (lane == 0)
+    *reinterpret_cast<uint32_t*>(a.scale_out + blk * a.sblk_bytes + 4 * r) = e | (e1 << 8) | (e2 << 16) | (e3 << 24);
 }
 
 }  // namespace
@@ -160,7 +207,10 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   }
   const dim3 grid((a.max_new_len + kFp8WavesPerBlock - 1) / kFp8WavesPerBlock, a.num_seqs);
   const dim3 block(64 * kFp8WavesPerBlock);
-  if (a.head_dim == 576)
+  if (a.mxfp4) {
+    if (a.head_dim != 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(append_mxfp4_kernel, grid, block, 0, stream, a);
+  } else if (a.head_dim == 576)
     hipLaunchKernelGGL(append_fp8_kernel<576>, grid, block, 0, stream, a);
   else if (a.head_dim == 128)
     hipLaunchKernelGGL(append_fp8_kernel<128>, grid, block, 0, stream, a);

@@ -11,7 +11,7 @@ namespace pa {
 namespace {
 
 // One thread per (token, head, 16-byte chunk).  GQA pools are [blocks][heads][bs][row];
-// FP8 pools are [blocks][bs][row] with one head.
+// FP8 and packed views have one head: row r of block b at k + b * blk_bytes + r * row_bytes.
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const int chunks = a.row_bytes / 16;
   const long total = (long)a.n_tokens * a.num_kv_heads * chunks;
@@ -22,8 +22,9 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     const int h = (int)((idx / chunks) % a.num_kv_heads);
     const int t = (int)(idx / ((long)chunks * a.num_kv_heads));
     const int pb = phys_block(a.bt_row, t / a.block_size, (int)n_lblocks, a.num_blocks);
-    const size_t src = (((size_t)(pb < 0 ? 0 : pb) * a.num_kv_heads + h) * a.block_size + t % a.block_size) *
-                           a.row_bytes + 16 * c;
+    const size_t b = (size_t)(pb < 0 ? 0 : pb), r = (size_t)(t % a.block_size);
+    const size_t src = a.is_fp8 ? b * a.blk_bytes + r * a.row_bytes + 16 * c
+                                : ((b * a.num_kv_heads + h) * a.block_size + r) * a.row_bytes + 16 * c;
     const size_t dst = ((size_t)t * a.num_kv_heads + h) * a.row_bytes + 16 * c;
     const u32x4 zero = {0, 0, 0, 0};
     st16(static_cast<uint8_t*>(a.k_out) + dst,
@@ -31,8 +32,8 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     if (!a.is_fp8)
       st16(static_cast<uint8_t*>(a.v_out) + dst,
            pb >= 0 ? ld16(static_cast<const uint8_t*>(a.v) + src) : zero);
-    if (a.is_fp8 && c == 0)
-      a.scale_out[t] = pb >= 0 ? a.scale[(size_t)pb * a.block_size + t % a.block_size] : 0.f;
+    if (a.is_fp8 && c == 0)   // the row's 4 scale bytes (fp32, or 4 E8M0 codes), bit for bit
+      a.scale_out[t] = pb >= 0 ? *reinterpret_cast<const float*>(a.sbase + b * a.sblk_bytes + 4 * r) : 0.f;
   }
 }
 

@@ -1,5 +1,7 @@
 // Indexer scores: I[i,t] = scale_t * sum_h w[i,h] * max(0, <q[i,h,:], e4m3(k_t)>) for
-// t <= pos(i), else -inf.
+// t <= pos(i), else -inf -- or, with the MXFP4 keys of the packed per-block layout (vLLM
+// AgentX article, "Hybrid KV cache management": the FP4 indexer), the same sum over the
+// decoded keys (E2M1 elements times their E8M0 group scale).
 //
 // Sources: vLLM AgentX article (news.ainew.jp), "DeepSeek V4" (the indexer has 64 heads
 // but yields one global top-k per token); GLM-5.3 report (aisoku.org), "What's new" (the
@@ -41,7 +43,11 @@ __device__ __forceinline__ int find_seq(const int32_t* q_start, int num_seqs, in
   return lo;
 }
 
-template <int NHT>   // head tiles of 16 (num_heads / 16)
+// FP4 (MXFP4 keys of the packed layout): a key row is 64 bytes, element 2j in the low
+// nibble of byte j, with one E8M0 scale code per 32 elements; the upcast to bf16 applies
+// the group scale (2^(e-127), built as the float with exponent field e), exact for codes
+// in [2, 252].  Keys carry no per-token scale (1 in the score).
+template <int NHT, bool FP4>   // head tiles of 16 (num_heads / 16)
 __global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t k_s[2][kKT * kKStride];
   __shared__ float sc_s[2][kKT];
@@ -100,9 +106,9 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
     // (tid + kThreads j) / 8, bytes 16 (tid % 8) ..
     constexpr int CPT = kKT * (kD / 16) / kThreads;
     static_assert(CPT * kThreads == kKT * (kD / 16), "whole chunks per thread");
-    const int key = tid >> 3, dc = tid & 7;
-    u32x4 raw[CPT];
-    float rsc[CPT];
+    const int key = tid >> 3, dc = tid & 7;   // dims 16 dc .. 16 dc + 15 of key `key`
+    u32x4 raw[CPT];                           // FP8: 16 codes; FP4: 16 codes in .x, .y
+    float rsc[CPT];                           // FP8: the key's scale; FP4: the group scale
     // A 64-key tile is exactly one 64-token block.  Its table entry is read one tile ahead
     // of its key loads (a vector load from an opaque copy of the index, so it is counted
     // with the key loads, in order, and never waits alone): the key loads of a tile never
@@ -120,25 +126,49 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
       for (int j = 0; j < CPT; ++j) {
         const int t = kb + key + (kThreads / 8) * j;
         const bool ok = pb >= 0 && t < total;
-        raw[j] = ok ? ld16(a.keys + ((size_t)pb * kBs + t % kBs) * kD + 16 * dc) : u32x4{0, 0, 0, 0};
-        if (dc == 0) rsc[j] = ok ? a.key_scale[(size_t)pb * kBs + t % kBs] : 0.f;
+        const size_t blk = (size_t)(ok ? pb : 0);
+        if constexpr (FP4) {
+          const u32x2 c = ok ? *reinterpret_cast<const u32x2*>(a.keys + blk * a.blk_bytes + (t % kBs) * (kD / 2) + 8 * dc)
+                             : u32x2{0, 0};
+          raw[j] = u32x4{c.x, c.y, 0, 0};
+          const uint32_t e = ok ? a.key_sbase[blk * a.sblk_bytes + (t % kBs) * 4 + (dc >> 1)] : 127u;
+          rsc[j] = __uint_as_float(e << 23);
+        } else {
+          raw[j] = ok ? ld16(a.keys + blk * a.blk_bytes + (t % kBs) * kD + 16 * dc) : u32x4{0, 0, 0, 0};
+          if (dc == 0)
+            rsc[j] = ok ? *reinterpret_cast<const float*>(a.key_sbase + blk * a.sblk_bytes + (t % kBs) * 4) : 0.f;
+        }
       }
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
         uint32_t bf[8];
+        if constexpr (FP4) {
+          // byte b of each word: elements 2b (low nibble) and 2b + 1
+          const uint32_t wx = raw[j].x, wy = raw[j].y;
+          const float sc = rsc[j];
+          bf[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wx, sc, 0));
+          bf[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wx, sc, 1));
+          bf[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wx, sc, 2));
+          bf[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wx, sc, 3));
+          bf[4] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wy, sc, 0));
+          bf[5] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wy, sc, 1));
+          bf[6] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wy, sc, 2));
+          bf[7] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wy, sc, 3));
+        } else {
 #pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4) {
-          const u32x2 c = fp8x4_to_bf16x4(raw[j][w4]);
-          bf[2 * w4] = c.x;
-          bf[2 * w4 + 1] = c.y;
+          for (int w4 = 0; w4 < 4; ++w4) {
+            const u32x2 c = fp8x4_to_bf16x4(raw[j][w4]);
+            bf[2 * w4] = c.x;
+            bf[2 * w4 + 1] = c.y;
+          }
         }
         const int kj = key + (kThreads / 8) * j;
         uint16_t* kp = k_s[buf] + kj * kKStride + 16 * dc;
         st16(kp, u32x4{bf[0], bf[1], bf[2], bf[3]});
         st16(kp + 8, u32x4{bf[4], bf[5], bf[6], bf[7]});
-        if (dc == 0) sc_s[buf][kj] = rsc[j];
+        if (dc == 0) sc_s[buf][kj] = FP4 ? 1.f : rsc[j];
       }
     };
     int id_next = -1;                                // raw table entry of tile tt+2
@@ -201,20 +231,25 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
   }
 }
 
+template <bool FP4>
+hipError_t launch_h(const IndexerArgs& a, unsigned grid, hipStream_t stream) {
+  switch (a.num_heads / 16) {
+    case 1: hipLaunchKernelGGL((indexer_kernel<1, FP4>), dim3(grid), dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((indexer_kernel<2, FP4>), dim3(grid), dim3(kThreads), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((indexer_kernel<3, FP4>), dim3(grid), dim3(kThreads), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((indexer_kernel<4, FP4>), dim3(grid), dim3(kThreads), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_indexer_scores(const IndexerArgs& a, hipStream_t stream) {
   const int n_chunks = (a.max_total_len + kChunk - 1) / kChunk;
   const unsigned grid = (unsigned)((a.n_q + kWaves - 1) / kWaves) * n_chunks;
   if (grid == 0) return hipSuccess;
-  switch (a.num_heads / 16) {
-    case 1: hipLaunchKernelGGL(indexer_kernel<1>, dim3(grid), dim3(kThreads), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(indexer_kernel<2>, dim3(grid), dim3(kThreads), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(indexer_kernel<3>, dim3(grid), dim3(kThreads), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(indexer_kernel<4>, dim3(grid), dim3(kThreads), 0, stream, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return a.fp4 ? launch_h<true>(a, grid, stream) : launch_h<false>(a, grid, stream);
 }
 
 }  // namespace pa

@@ -147,7 +147,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
   const int32_t* bt_row;
   const int32_t* sel_g = nullptr;
   const uint8_t* kv;
-  const float* kv_scale;
+  const uint8_t* ksb;                               // latent scales (see MlaDecodeArgs)
+  int64_t blk_bytes, sblk_bytes;
   int Hq, n_keys, k_begin = 0, n_lblocks, L = 0, T = 1, row0, unit = 0, unit_split = 0;
   int lb_base = 0, n_bt, num_blocks;
   float scale_log2;
@@ -160,7 +161,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
     row0 = (bid % rblocks) * RW;
     unit = i;
     qbase = sa.q + (size_t)i * Hq * kDqk;
-    kv = sa.kv; kv_scale = sa.kv_scale; num_blocks = sa.num_blocks;
+    kv = sa.kv; ksb = sa.kv_sbase; num_blocks = sa.num_blocks;
+    blk_bytes = sa.blk_bytes; sblk_bytes = sa.sblk_bytes;
     bt_row = sa.bt + (size_t)sa.q_seq[i] * sa.bt_stride;
     sel_g = sa.topk + (size_t)i * sa.k;
     n_keys = sa.k;
@@ -186,7 +188,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
     if (k_begin >= L) return;                         // uniform for the workgroup
     n_keys = min(L - k_begin, kDecodeSplitMla);
     qbase = da.q + (size_t)unit * rows * kDqk;
-    kv = da.kv; kv_scale = da.kv_scale; num_blocks = da.num_blocks;
+    kv = da.kv; ksb = da.kv_sbase; num_blocks = da.num_blocks;
+    blk_bytes = da.blk_bytes; sblk_bytes = da.sblk_bytes;
     bt_row = da.bt + (size_t)unit * da.bt_stride;
     n_lblocks = (L + kBs - 1) / kBs;
     lb_base = k_begin / kBs;
@@ -249,14 +252,15 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
       // rows are one contiguous 18,432-byte span of one block
       const int pos0 = k_begin + kb;
       const int pb = bt_s[pos0 / kBs - lb_base];
-      const uint8_t* span = pb >= 0 ? kv + ((size_t)pb * kBs + pos0 % kBs) * kDqk : kv;
+      const uint8_t* span = pb >= 0 ? kv + (size_t)pb * blk_bytes + (pos0 % kBs) * kDqk : kv;
 #pragma unroll
       for (int m = 0; m < kLoadsPerWave; ++m) {
         const int j = wave + NW * m;
         if (j < kWaveLoads) dma16(pb >= 0 ? span + 16 * (64 * j + ln) : kv, lds_u32(R) + 1024 * j);
       }
       if (wave == NW - 1 && ln < kKT) {
-        dma4(pb >= 0 ? kv_scale + (size_t)pb * kBs + pos0 % kBs + ln : kv_scale, lds_u32(RS));
+        dma4(pb >= 0 ? reinterpret_cast<const float*>(ksb + (size_t)pb * sblk_bytes) + pos0 % kBs + ln
+                     : reinterpret_cast<const float*>(ksb), lds_u32(RS));
         RK[ln] = (pb >= 0 && kb + ln < n_keys) ? pos0 + ln : -1;
       }
     } else {
@@ -272,11 +276,15 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaDecodeArgs da, Spars
       for (int m = 0; m < kLoadsPerWave; ++m) {
         const int j = wave + NW * m;
         const int dc = (64 * j + ln) % (kDqk / 16);
-        if (j < kWaveLoads) dma16(prow[m] >= 0 ? kv + (size_t)prow[m] * kDqk + 16 * dc : kv, lds_u32(R) + 1024 * j);
+        const int pr = prow[m];
+        if (j < kWaveLoads)
+          dma16(pr >= 0 ? kv + (size_t)(pr >> 6) * blk_bytes + (pr & (kBs - 1)) * kDqk + 16 * dc : kv,
+                lds_u32(R) + 1024 * j);
       }
       if (wave == NW - 1 && ln < kKT) {
         const int pr = key_row(kb + ln);
-        dma4(pr >= 0 ? kv_scale + pr : kv_scale, lds_u32(RS));
+        dma4(pr >= 0 ? reinterpret_cast<const float*>(ksb + (size_t)(pr >> 6) * sblk_bytes) + (pr & (kBs - 1))
+                     : reinterpret_cast<const float*>(ksb), lds_u32(RS));
         RK[ln] = pr;
       }
     }

@@ -43,9 +43,21 @@ pa_status check_gqa_pool(const pa_kv_pool* p) {
   return PA_OK;
 }
 
+bool is_packed_pool(const pa_kv_pool* p) { return p->kv_dtype == PA_PACKED_MLA; }
+
 pa_status check_fp8_pool(const pa_kv_pool* p, int d_qk, int d_v, const char* what) {
   if (p == nullptr) return fail(PA_ERR_INVALID_ARG, "%s pool is NULL", what);
-  if (p->kv_dtype != PA_FP8_E4M3) return fail(PA_ERR_UNSUPPORTED, "%s pool must be PA_FP8_E4M3", what);
+  if (is_packed_pool(p)) {
+    if (p->block_size != 64 || p->num_kv_heads != 1 || p->head_dim_qk != d_qk || p->head_dim_v != d_v)
+      return fail(PA_ERR_UNSUPPORTED, "%s view of a packed pool must be block 64, one head, dims %d/%d", what,
+                  d_qk, d_v);
+    if (p->num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_blocks must be >= 1");
+    if (p->num_blocks > INT32_MAX / 64) return fail(PA_ERR_UNSUPPORTED, "%s pool: num_blocks * 64 rows must fit in int32", what);
+    if (p->k == nullptr) return fail(PA_ERR_INVALID_ARG, "%s packed pool k is NULL", what);
+    if (!aligned(p->k, 16)) return fail(PA_ERR_INVALID_ARG, "%s packed pool must be 16-byte aligned", what);
+    return PA_OK;
+  }
+  if (p->kv_dtype != PA_FP8_E4M3) return fail(PA_ERR_UNSUPPORTED, "%s pool must be PA_FP8_E4M3 or PA_PACKED_MLA", what);
   if (p->block_size != 64) return fail(PA_ERR_UNSUPPORTED, "%s pool block_size must be 64 (got %d)", what, p->block_size);
   if (p->num_kv_heads != 1) return fail(PA_ERR_UNSUPPORTED, "%s pool must have num_kv_heads == 1", what);
   if (p->head_dim_qk != d_qk || p->head_dim_v != d_v)
@@ -56,6 +68,42 @@ pa_status check_fp8_pool(const pa_kv_pool* p, int d_qk, int d_v, const char* wha
   if (p->k == nullptr || p->scale == nullptr) return fail(PA_ERR_INVALID_ARG, "%s pool k/scale is NULL", what);
   if (!aligned(p->k, 16) || !aligned(p->scale, 4)) return fail(PA_ERR_INVALID_ARG, "%s pool must be 16-byte aligned", what);
   return PA_OK;
+}
+
+// Rows of one cache group of an FP8 pool or of a view of a packed pool: row r of block b
+// at rows + b * blk + r * row_bytes, its 4 scale bytes at scales + b * sblk + 4 r.
+struct RowView {
+  const uint8_t* rows;
+  const uint8_t* scales;
+  int64_t blk, sblk;
+  int32_t row_bytes, fp4;
+};
+
+constexpr int64_t kPackedBlock = 41472, kPackedLatentScale = 36864, kPackedKeys = 37120, kPackedKeyScales = 41216;
+
+RowView row_view(const pa_kv_pool* p) {
+  RowView v{};
+  const uint8_t* base = static_cast<const uint8_t*>(p->k);
+  if (is_packed_pool(p)) {
+    v.blk = v.sblk = kPackedBlock;
+    if (p->head_dim_qk == 576) {
+      v.rows = base;
+      v.scales = base + kPackedLatentScale;
+      v.row_bytes = 576;
+    } else {
+      v.rows = base + kPackedKeys;
+      v.scales = base + kPackedKeyScales;
+      v.row_bytes = 64;
+      v.fp4 = 1;
+    }
+    return v;
+  }
+  v.rows = base;
+  v.scales = reinterpret_cast<const uint8_t*>(p->scale);
+  v.blk = (int64_t)p->block_size * p->head_dim_qk;
+  v.sblk = (int64_t)p->block_size * 4;
+  v.row_bytes = p->head_dim_qk;
+  return v;
 }
 
 pa_status launched(hipError_t e, const char* what) {
@@ -347,8 +395,11 @@ static pa_status decode_impl(const void* q, const pa_kv_pool* pool, const int32_
   } else {
     pa::MlaDecodeArgs a{};
     a.q = static_cast<const uint16_t*>(q);
-    a.kv = static_cast<const uint8_t*>(pool->k);
-    a.kv_scale = pool->scale;
+    const RowView rv = row_view(pool);
+    a.kv = rv.rows;
+    a.kv_sbase = rv.scales;
+    a.blk_bytes = rv.blk;
+    a.sblk_bytes = rv.sblk;
     a.bt = block_table;
     a.context_len = context_len;
     a.part_o = part_o;
@@ -482,8 +533,12 @@ pa_status mla_indexer_topk(const void* q_idx, const float* w, const pa_kv_pool* 
   pa::IndexerArgs a{};
   a.q_idx = static_cast<const uint16_t*>(q_idx);
   a.w = w;
-  a.keys = static_cast<const uint8_t*>(idx_pool->k);
-  a.key_scale = idx_pool->scale;
+  const RowView rv = row_view(idx_pool);
+  a.keys = rv.rows;
+  a.key_sbase = rv.scales;
+  a.blk_bytes = rv.blk;
+  a.sblk_bytes = rv.sblk;
+  a.fp4 = rv.fp4;
   a.bt = block_table;
   a.cached_len = cached_len;
   a.new_len = new_len;
@@ -534,8 +589,11 @@ pa_status sparse_mla_attn(const void* q, const pa_kv_pool* pool, const int32_t* 
   (void)hipGetLastError();
   pa::SparseMlaArgs a{};
   a.q = static_cast<const uint16_t*>(q);
-  a.kv = static_cast<const uint8_t*>(pool->k);
-  a.kv_scale = pool->scale;
+  const RowView rv = row_view(pool);
+  a.kv = rv.rows;
+  a.kv_sbase = rv.scales;
+  a.blk_bytes = rv.blk;
+  a.sblk_bytes = rv.sblk;
   a.bt = block_table;
   a.q_seq = q_seq;
   a.topk = topk_idx;
@@ -557,7 +615,7 @@ pa_status paged_kv_append(const pa_kv_pool* pool, const int32_t* block_table, in
                           const void* v_new, hipStream_t stream) {
   g_detail[0] = 0;
   if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
-  const bool fp8 = pool->kv_dtype == PA_FP8_E4M3;
+  const bool fp8 = pool->kv_dtype == PA_FP8_E4M3 || is_packed_pool(pool);
   if (fp8) {
     if (pool->head_dim_qk == 576)
       PA_TRY(check_fp8_pool(pool, 576, 512, "MLA"));
@@ -587,8 +645,12 @@ pa_status paged_kv_append(const pa_kv_pool* pool, const int32_t* block_table, in
   // the pool descriptor's pointers are const for the attention calls; the append is the
   // one call that writes through them
   if (fp8) {
-    a.fp8_out = static_cast<uint8_t*>(const_cast<void*>(pool->k));
-    a.scale_out = const_cast<float*>(pool->scale);
+    const RowView rv = row_view(pool);
+    a.fp8_out = const_cast<uint8_t*>(rv.rows);
+    a.scale_out = const_cast<uint8_t*>(rv.scales);
+    a.blk_bytes = rv.blk;
+    a.sblk_bytes = rv.sblk;
+    a.mxfp4 = rv.fp4;
   } else {
     a.k_out = static_cast<uint16_t*>(const_cast<void*>(pool->k));
     a.v_out = static_cast<uint16_t*>(const_cast<void*>(pool->v));
@@ -613,11 +675,15 @@ pa_status pa_test_gather_kv(const pa_kv_pool* pool, const int32_t* block_table, 
   g_detail[0] = 0;
   if (pool == nullptr || block_table == nullptr || k_out == nullptr)
     return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
-  const bool fp8 = pool->kv_dtype == PA_FP8_E4M3;
+  const bool fp8 = pool->kv_dtype == PA_FP8_E4M3 || is_packed_pool(pool);
   if (fp8) {
-    if (pool->k == nullptr || pool->scale == nullptr || scale_out == nullptr || pool->num_kv_heads != 1 ||
-        pool->head_dim_qk % 16 != 0 || pool->block_size < 1)
+    if (is_packed_pool(pool)) {
+      PA_TRY(check_fp8_pool(pool, pool->head_dim_qk == 576 ? 576 : 128, pool->head_dim_qk == 576 ? 512 : 0, "gather"));
+      if (scale_out == nullptr) return fail(PA_ERR_INVALID_ARG, "scale_out is NULL");
+    } else if (pool->k == nullptr || pool->scale == nullptr || scale_out == nullptr || pool->num_kv_heads != 1 ||
+               pool->head_dim_qk % 16 != 0 || pool->block_size < 1) {
       return fail(PA_ERR_INVALID_ARG, "bad FP8 pool for gather");
+    }
   } else {
     PA_TRY(check_gqa_pool(pool));
     if (v_out == nullptr) return fail(PA_ERR_INVALID_ARG, "v_out is NULL");
@@ -629,7 +695,13 @@ pa_status pa_test_gather_kv(const pa_kv_pool* pool, const int32_t* block_table, 
   pa::GatherArgs a{};
   a.k = pool->k;
   a.v = pool->v;
-  a.scale = pool->scale;
+  if (fp8) {
+    const RowView rv = row_view(pool);
+    a.k = rv.rows;
+    a.sbase = rv.scales;
+    a.blk_bytes = rv.blk;
+    a.sblk_bytes = rv.sblk;
+  }
   a.bt_row = block_table + (size_t)seq * bt_stride;
   a.k_out = k_out;
   a.v_out = v_out;
@@ -638,7 +710,7 @@ pa_status pa_test_gather_kv(const pa_kv_pool* pool, const int32_t* block_table, 
   a.num_blocks = pool->num_blocks;
   a.block_size = pool->block_size;
   a.num_kv_heads = pool->num_kv_heads;
-  a.row_bytes = fp8 ? pool->head_dim_qk : pool->head_dim_qk * 2;
+  a.row_bytes = fp8 ? row_view(pool).row_bytes : pool->head_dim_qk * 2;
   a.is_fp8 = fp8 ? 1 : 0;
   return launched(pa::launch_gather(a, stream), "gather launch");
 }

@@ -102,10 +102,15 @@ struct CombineArgs {
   int32_t pf_max_new, pf_max_total;
 };
 
+// FP8 latent rows of a paged pool: row r of block b at kv + b * blk_bytes + r * 576, its
+// fp32 scale at kv_sbase + b * sblk_bytes + 4 r.  Separate pools: blk_bytes 36,864,
+// sblk_bytes 256; the packed per-block layout: both 41,472 (scales at byte 36,864 of a
+// block).
 struct MlaDecodeArgs {
   const uint16_t* q;            // [S][T][Hq][576]
-  const uint8_t* kv;            // [NB][64][576]
-  const float* kv_scale;        // [NB][64]
+  const uint8_t* kv;            // latent rows (see above)
+  const uint8_t* kv_sbase;      // latent scales
+  int64_t blk_bytes, sblk_bytes;
   const int32_t* bt;
   const int32_t* context_len;
   float* part_o;                // [S][max_splits][T*Hq][512]
@@ -116,8 +121,9 @@ struct MlaDecodeArgs {
 
 struct SparseMlaArgs {
   const uint16_t* q;            // [n_q][Hq][576]
-  const uint8_t* kv;
-  const float* kv_scale;
+  const uint8_t* kv;            // as MlaDecodeArgs
+  const uint8_t* kv_sbase;
+  int64_t blk_bytes, sblk_bytes;
   const int32_t* bt;
   const int32_t* q_seq;
   const int32_t* topk;          // [n_q][k]
@@ -130,8 +136,14 @@ struct SparseMlaArgs {
 struct IndexerArgs {
   const uint16_t* q_idx;        // [n_q][H][128]
   const float* w;               // [n_q][H]
-  const uint8_t* keys;          // [NB][64][128]
-  const float* key_scale;       // [NB][64]
+  // Key row r of block b at keys + b * blk_bytes + r * row_bytes, its scale at
+  // key_sbase + b * sblk_bytes + 4 r.  FP8 keys (fp4 = 0): 128-byte rows, one fp32 scale
+  // per key.  MXFP4 keys of the packed layout (fp4 = 1): 64-byte rows (element 2j in the
+  // low nibble of byte j), four E8M0 codes per key (one per 32 elements).
+  const uint8_t* keys;
+  const uint8_t* key_sbase;
+  int64_t blk_bytes, sblk_bytes;
+  int32_t fp4;
   const int32_t* bt;
   const int32_t* cached_len;
   const int32_t* new_len;
@@ -152,7 +164,8 @@ struct TopkArgs {
 struct GatherArgs {
   const void* k;
   const void* v;
-  const float* scale;
+  const uint8_t* sbase;         // FP8 / packed views: scale of row r of block b at
+  int64_t blk_bytes, sblk_bytes;  // sbase + b * sblk_bytes + 4 r; row at k + b * blk_bytes + r * row_bytes
   const int32_t* bt_row;
   void* k_out;
   void* v_out;
@@ -170,8 +183,10 @@ struct AppendArgs {
   const int32_t* q_start;
   uint16_t* k_out;              // GQA pool K / V [NB][Hkv][bs][d]
   uint16_t* v_out;
-  uint8_t* fp8_out;             // FP8 pool [NB][bs][D]
-  float* scale_out;             // [NB][bs]
+  uint8_t* fp8_out;             // FP8 / packed rows: row r of block b at fp8_out + b * blk_bytes + r * row_bytes
+  uint8_t* scale_out;           // its scale (fp32, or 4 E8M0 codes) at scale_out + b * sblk_bytes + 4 r
+  int64_t blk_bytes, sblk_bytes;
+  int32_t mxfp4;                // 1: MXFP4 rows (the packed layout's index keys), else FP8
   int32_t bt_stride, num_seqs, n_tokens, max_new_len, num_blocks, block_size, num_kv_heads;
   int32_t head_dim;             // d (GQA) or D (FP8)
   int32_t is_fp8;
