@@ -9,8 +9,9 @@ contexts log-uniform in [4,000, 142,000], sequences in 8 sessions whose first 90
 blocks are shared (same physical blocks).  Inputs are resident in HBM before timing.
 
 Timing: W untimed warm-up steps, then K timed steps; before every step a 1 GiB
-device-to-device copy evicts L2 and the MALL (so reuse within a call counts, reuse across
-calls does not), and HIP events on the launch stream time each step alone.  ms_per_step
+device-to-device copy followed by a read of another 1 GiB evicts L2 and the MALL (so reuse
+within a call counts, reuse across calls does not, and no dirty flush data is written back
+inside the timed step), and HIP events on the launch stream time each step alone.  ms_per_step
 is the median step; the minimum and mean are reported beside it, and the library's own
 events time each kernel launch.
 
@@ -54,13 +55,17 @@ _FLUSH = []
 
 
 def _flush():
-    """Evict L2 and the MALL (256 MB) between timed steps: a 1 GiB device copy, on the
-    launch stream, outside the timed events."""
+    """Evict L2 and the MALL (256 MB) between timed steps, on the launch stream, outside the
+    timed events: overwrite 1 GiB (a device copy), then read another 1 GiB, so the caches
+    hold only clean lines of unrelated data and the timed kernel neither hits on its own
+    previous data nor pays for writing back the flush's dirty lines."""
     import torch
     if not _FLUSH:
         _FLUSH.append(torch.ones(1 << 30, dtype=torch.uint8, device="cuda"))
         _FLUSH.append(torch.empty(1 << 30, dtype=torch.uint8, device="cuda"))
+        _FLUSH.append(torch.ones(1 << 28, dtype=torch.float32, device="cuda"))
     _FLUSH[1].copy_(_FLUSH[0])
+    _FLUSH[2].sum()
 
 
 def timed_steps(step, steps, warmup):

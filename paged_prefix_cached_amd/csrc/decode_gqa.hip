@@ -14,28 +14,15 @@
 //      the DISTINCT block pairs its members reference, each with the set of members that
 //      share it and the number of its keys that hold data.  Blocks that forked sequences
 //      share become one pass for all of them: fetched from HBM once, not once per member.
-//   2. decode_units_kernel cuts each group's pass list into units of at most kUnitPasses
-//      passes, numbers them and resets the work queue.  A unit's length is fixed by its
-//      passes, not by its keys, so units where members diverge (one pass per member per
-//      tile) cost the same as units over a shared prefix.
-//   3. gqa_decode_kernel: a persistent grid whose workgroups take (unit, KV head) items
-//      from an atomic queue until it is empty.  The four waves of a workgroup take the
-//      unit's passes round robin; per pass a wave
-//        * has issued the pass's K and V loads while the previous pass was computed
-//          (register double buffering: one pass always in flight per wave);
-//        * uses K straight from registers as the A operand of S^T = K Q^T (lane l: key
-//          l%32); Q^T fragments come from LDS (B operand, lane = query row);
-//        * masks rows whose member does not share the pass and keys past each row's
-//          position, then updates its online softmax in-lane (one xor-32 step per row);
-//        * writes V (bf16; keys without data zeroed) row-major into its LDS slice and
-//          accumulates O^T += V^T P^T with two v_mfma_f32_32x32x16_bf16, P split into bf16
-//          hi + lo parts (P keeps ~16 significant bits: one bf16 would cost ~1.5e-3
-//          relative error in O); the V^T fragments come from ds_read_b64_tr_b16
-//          transpose reads, P straight from registers.
-//      The accumulator is rescaled only when a row's running maximum grows.  The wave
-//      states are merged pairwise through LDS in a fixed order and the unit's normalised
-//      partial output and log2-sum-exp go to the workspace.
-//   4. combine_kernel merges each row's unit partials in unit order.
+//   2. decode_scan_kernel numbers the passes of all groups consecutively (region by
+//      region) and the pieces that the attention grid cuts them into.
+//   3. gqa_decode_kernel: one workgroup per compute unit, each taking an equal share of
+//      the pass list -- every pass costs the same (two blocks of K and V per KV head), so
+//      the shares finish together -- with one wave per KV head, so the eight waves read
+//      the same blocks for all heads and never wait for one another.  Each piece (a
+//      group's passes inside one workgroup's share) yields a normalised partial output
+//      and log2-sum-exp per head.
+//   4. combine_kernel merges each row's partials in pass order.
 // Every partition depends on the inputs only, so results are identical run to run.
 #include <algorithm>
 
@@ -53,19 +40,19 @@ GqaDecodeDims gqa_decode_dims(int num_seqs, int q_per_seq, int num_q_heads, int 
   const long n_tiles = (max_context_len + 31) / 32;
   d.n_chunks = (int)((n_tiles + kPlanTiles - 1) / kPlanTiles);
   d.region_cap = kPlanTiles * d.members;
-  // a member references at most one distinct pair per tile of its context
-  const long regions = (long)d.n_groups * d.n_chunks;
-  d.units_cap = (int)(((long)num_seqs * n_tiles + kUnitPasses - 1) / kUnitPasses + regions);
+  d.grid = device_cus();
+  d.subs = (num_kv_heads < 8 && 8 % num_kv_heads == 0) ? 8 / num_kv_heads : 1;
+  // pieces: every region's passes cut at the workgroup boundaries
+  d.pieces_cap = d.n_groups * d.n_chunks + d.grid - 1;
   return d;
 }
 
 namespace {
 
-// Waves per attention workgroup; 8 / kWaves workgroups share a compute unit.
-constexpr int kWaves = PA_DECODE_WAVES;
+// Waves per attention workgroup (one workgroup per compute unit, two waves per SIMD): one
+// per KV head of the 8, or 8 / Hkv sub-ranges per head for fewer heads.
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-static_assert(kWaves == 2 || kWaves == 4 || kWaves == 8, "waves per workgroup");
-static_assert(kUnitPasses <= kThreads, "a unit's descriptors are staged one per thread");
 constexpr int kTile = 32;               // keys per pass (two 16-token blocks)
 
 // ---------------------------------------------------------------------------------
@@ -161,58 +148,93 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(GqaDecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------------
-// 2. Units: region r (group r / n_chunks) holds n_passes[r] passes; it is cut into
-// ceil(n / kUnitPasses) units, numbered in region order.  One workgroup.
-__global__ __launch_bounds__(1024) void decode_units_kernel(GqaDecodeArgs a) {
-  __shared__ int wsum[16];
+// 2. Scan (one workgroup): region_start[r] = passes of the regions before r in region order
+// (the compact pass numbering; region_start[R] = P, the total), and piece_start[r] = pieces
+// before region r.  The attention grid splits [0, P) evenly over N = min(grid, P)
+// workgroups: workgroup w < N takes passes [floor(w P / N), floor((w + 1) P / N)), never
+// an empty range (P / N >= 1).  A piece is a region's share of one workgroup's range, so
+// region r holds wg_of(last) - wg_of(first) + 1 pieces (0 when it has no pass), and the
+// pieces of a group are numbered consecutively in pass order.
+// wg_of(x): the workgroup whose range holds pass x, max{w : floor(w P / N) <= x}.
+__device__ __forceinline__ int wg_of(long x, long P, long N) { return (int)(((x + 1) * N - 1) / P); }
+__device__ __forceinline__ long active_wgs(long grid, long P) { return grid < P ? grid : P; }
+
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int off = x - v, t = 0;
+  for (int w = 0; w < 16; ++w) {
+    off += w < wave ? wsum[w] : 0;
+    t += wsum[w];
+  }
+  __syncthreads();
+  *total = t;
+  return off;
+}
+
+__global__ __launch_bounds__(1024) void decode_scan_kernel(GqaDecodeArgs a) {
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x;
   const int n = a.dims.n_groups * a.dims.n_chunks;
   int running = 0;
   for (int base = 0; base < n; base += 1024) {
     const int r = base + tid;
-    const int np = r < n ? a.n_passes[r] : 0;
-    const int nu = (np + kUnitPasses - 1) / kUnitPasses;
-    int x = nu;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o);
-      if (lane >= o) x += y;
-    }
-    if (lane == 63) wsum[wave] = x;
-    __syncthreads();
-    int off = x - nu, total = 0;
-    for (int w = 0; w < 16; ++w) {
-      off += w < wave ? wsum[w] : 0;
-      total += wsum[w];
-    }
-    __syncthreads();
-    if (r < n) {
-      const int u0 = running + off;
-      a.unit_start[r] = u0;
-      const uint32_t g = (uint32_t)(r / a.dims.n_chunks);
-      const uint32_t p0 = (uint32_t)((size_t)r * a.dims.region_cap);
-      for (int k = 0; k < nu; ++k)
-        st16(a.units + (size_t)(u0 + k) * 4,
-             u32x4{g, p0 + (uint32_t)(k * kUnitPasses), p0 + (uint32_t)min((k + 1) * kUnitPasses, np), 0u});
-    }
+    int total;
+    const int off = block_exclusive_scan(r < n ? a.n_passes[r] : 0, wsum, &total);
+    if (r < n) a.region_start[r] = running + off;
     running += total;
   }
-  if (tid == 0) {
-    a.unit_start[n] = running;
-    a.queue[0] = 0;
-    a.queue[1] = running * a.num_kv_heads;
+  if (tid == 0) a.region_start[n] = running;
+  __syncthreads();
+  const long P = running, N = active_wgs(a.dims.grid, P);
+  int pieces = 0;
+  for (int base = 0; base < n; base += 1024) {
+    const int r = base + tid;
+    int cnt = 0;
+    if (r < n) {
+      const int s0 = a.region_start[r], s1 = a.region_start[r + 1];
+      cnt = s1 > s0 ? wg_of(s1 - 1, P, N) - wg_of(s0, P, N) + 1 : 0;
+    }
+    int total;
+    const int off = block_exclusive_scan(cnt, wsum, &total);
+    if (r < n) a.piece_start[r] = pieces + off;
+    pieces += total;
   }
+  if (tid == 0) a.piece_start[n] = pieces;
 }
 
 // ---------------------------------------------------------------------------------
-// 3. Attention over the passes of one unit and KV head per workgroup iteration.
+// 3. Attention: workgroup w of N = min(grid, P) takes the passes [floor(w P / N), floor((w + 1) P / N))
+// of the compact pass list -- equal shares, so the workgroups finish together -- and
+// walks them region by region (a piece per region it meets).  Each wave takes one KV
+// head (and, when the heads are fewer than 8 and divide 8, one of 8 / Hkv equal
+// sub-ranges of the piece), so the 8 waves of a workgroup read the same blocks for all
+// heads at once (a block's K, or V, is Hkv * 4 KB contiguous) and never wait for one
+// another: there is no barrier and no merge across waves.  Per pass a wave
+//   * has issued the pass's K and V loads while the previous pass was computed
+//     (register double buffering), and its descriptor one pass earlier still;
+//   * uses K straight from registers as the A operand of S^T = K Q^T; the Q^T fragments
+//     (B operand, lane = query row) come from the wave's own LDS copy of its 32 rows;
+//   * masks rows whose member does not share the pass and keys past each row's
+//     position, then updates its online softmax in-lane (one xor-32 step per row);
+//   * writes V (bf16; keys without data zeroed) row-major into its own LDS slice and
+//     accumulates O^T += V^T P^T with two v_mfma_f32_32x32x16_bf16, P split into bf16
+//     hi + lo parts (~16 significant bits), V^T from ds_read_b64_tr_b16 transpose reads.
+// At a piece's end the wave writes the normalised partial output and log2-sum-exp of its
+// 32 rows to slot ((piece * subs + sub) * Hkv + head).
 template <int D>
 struct DecodeSmem {
   static constexpr int kVStride = D + 16;   // bf16 per V row: 32-byte pad, conflict-free tr reads
   static constexpr int kQStride = D + 8;    // bf16 per Q row: 16-byte pad
-  uint16_t v[kWaves][kTile * kVStride];
-  uint16_t q[32 * kQStride];
-  u32x4 desc[kUnitPasses];
+  uint16_t v[kWaves][kTile * kVStride];     // each wave's own slices
+  uint16_t q[kWaves][32 * kQStride];
 };
 
 struct Pass {
@@ -228,246 +250,244 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int VG = D / 64;   // (4 keys x 8 dims) V groups per lane per pass
   using Sm = DecodeSmem<D>;
   __shared__ __attribute__((aligned(16))) Sm sm;
-  __shared__ float mrg_ml[kWaves / 2][2][32];
-  __shared__ int item_s;
+  __shared__ int prog[kWaves];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (lane == 0) prog[wave] = 0;
+  int done = 0;
   const int c32 = lane & 31, h32 = lane >> 5;
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
   const int G = Hq / Hkv, T = a.q_per_seq, R = T * G;
-  const int M = a.dims.members;
+  const int M = a.dims.members, NS = a.dims.subs;
   const int m = c32 / R, rr = c32 % R;
   const int t = rr / G, hh = rr % G;
-  const int n_items = a.queue[1];
   const size_t head_stride = (size_t)16 * D;
   uint16_t* vs = sm.v[wave];
+  uint16_t* qs = sm.q[wave];
+  const int n_regions = a.dims.n_groups * a.dims.n_chunks;
+  const long P = a.region_start[n_regions];
+  const long N = active_wgs(gridDim.x, P);
+  const int w = blockIdx.x;
+  if (w >= N) return;                               // fewer passes than workgroups
+  const int lo = (int)((long)w * P / N), hi = (int)((long)(w + 1) * P / N);
+  // this wave's (head, sub-range): NS = 8 / Hkv sub-ranges when Hkv divides 8, else one
+  // and heads wave, wave + 8, ...
+  const int sub = NS > 1 ? wave / Hkv : 0;
+  const int h_first = NS > 1 ? wave % Hkv : wave;
+  // first region holding pass lo: the first r with region_start[r + 1] > lo
+  int rlo = 0, rhi = n_regions - 1;
+  while (rlo < rhi) {
+    const int mid = (rlo + rhi) >> 1;
+    if (a.region_start[mid + 1] > lo) rhi = mid; else rlo = mid + 1;
+  }
+  const int m16 = lane & 15, gq = (lane >> 4) & 1;
 
-  for (;;) {
-    if (tid == 0) item_s = atomicAdd(&a.queue[0], 1);
-    __syncthreads();
-    const int item = __builtin_amdgcn_readfirstlane(item_s);
-    if (item >= n_items) break;                     // uniform for the whole workgroup
-    const int g = item % Hkv, unit = item / Hkv;
-    const u32x4 ud = ld16(a.units + (size_t)unit * 4);
-    const int grp = (int)__builtin_amdgcn_readfirstlane(ud.x);
-    const int p_begin = (int)__builtin_amdgcn_readfirstlane(ud.y);
-    const int np = (int)__builtin_amdgcn_readfirstlane(ud.z) - p_begin;
-    const int s0 = grp * M;
-
-    // ---- this lane's query row: member m, token t, head hh
-    const int s = s0 + m;
+  for (int r = rlo; r < n_regions; ++r) {
+    const int s_r = a.region_start[r], s_r1 = a.region_start[r + 1];
+    if (s_r >= hi) break;
+    const int x0 = max(s_r, lo), x1 = min(s_r1, hi);
+    if (x0 >= x1) continue;                         // a region with no pass
+    const int grp = r / a.dims.n_chunks;
+    const int piece = a.piece_start[r] + (w - wg_of(s_r, P, N));
+    const size_t pass_base = (size_t)r * a.dims.region_cap;
+    const int px0 = x0 - s_r + (int)((long)(x1 - x0) * sub / NS);
+    const int px1 = x0 - s_r + (int)((long)(x1 - x0) * (sub + 1) / NS);
+    const int s = grp * M + m;
     const bool row_ok = (m < M) && (s < a.num_seqs);
     const int L = row_ok ? min(max(a.context_len[s], 0), a.max_context_len) : 0;
     const int pos = L - T + t;                      // keys <= pos are visible
 
-    // ---- the unit's pass descriptors and the group's 32 query rows -> LDS
-    if (tid < np) sm.desc[tid] = ld16(a.passes + ((size_t)p_begin + tid) * 4);
-    for (int c = tid; c < 32 * DC; c += kThreads) {
-      const int r = c / DC, dc = c % DC;
-      const int mr = r / R, rr2 = r % R, sr = s0 + mr;
-      u32x4 v = {0, 0, 0, 0};
-      if (mr < M && sr < a.num_seqs)
-        v = ld16(a.q + ((size_t)(sr * T + rr2 / G) * Hq + g * G + rr2 % G) * D + 8 * dc);
-      st16(sm.q + r * Sm::kQStride + 8 * dc, v);
-    }
-    __syncthreads();
+    for (int g = h_first; g < Hkv; g += (NS > 1 ? Hkv : kWaves)) {
+      const uint16_t* qrow = qs + c32 * Sm::kQStride + 8 * h32;
+      f32x16 acc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+      float m_run = -INFINITY, l_run = 0.f;
 
-    f32x16 acc[MT];
+      // ---- passes px0 .. px1 - 1 of region r; the descriptor of the next pass to issue
+      // is loaded one pass ahead
+      int it = px0;
+      u32x4 dnext = it < px1 ? ld16(a.passes + (pass_base + it) * 4) : u32x4{0, 0, 0, 0};
+      auto next_pass = [&](Pass& Pp) -> bool {
+        if (it >= px1) return false;
+        const u32x4 d = dnext;
+        ++it;
+        if (it < px1) dnext = ld16(a.passes + (pass_base + it) * 4);
+        const uint32_t d0 = __builtin_amdgcn_readfirstlane(d.x);
+        Pp.kb = (int)(d0 & ~31u);
+        Pp.nv = (int)(d0 & 31u) + 1;
+        Pp.bA = (int)__builtin_amdgcn_readfirstlane(d.y);
+        Pp.bB = (int)__builtin_amdgcn_readfirstlane(d.z);
+        const uint32_t mask = __builtin_amdgcn_readfirstlane(d.w);
+        Pp.in = row_ok && ((mask >> m) & 1u);
+        return true;
+      };
+      // K rows straight into the A operand (lane: key c32 of the pass); V as 4 keys x 8 dims.
+      // Interior passes (both blocks present, all 32 keys hold data) take an unconditional path.
+      auto issue = [&](const Pass& Pp, u32x4 (&kf)[KS], u32x4 (&vr)[VG][4]) {
+        if (Pp.bA >= 0 && Pp.bB >= 0 && Pp.nv == kTile) {
+          const int blk = c32 < 16 ? Pp.bA : Pp.bB;
+          const uint16_t* kp = a.k + ((size_t)blk * Hkv + g) * head_stride + (size_t)(c32 & 15) * D + 8 * h32;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+          for (int ks = 0; ks < KS; ++ks) kf[ks] = ld16(kp + 16 * ks);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
-
-    // ---- this wave's passes: wave, wave + 4, ... of the unit
-    int it = wave;
-    auto next_pass = [&](Pass& P) -> bool {
-      if (it >= np) return false;
-      const u32x4 d = sm.desc[it];
-      it += kWaves;
-      const uint32_t d0 = __builtin_amdgcn_readfirstlane(d.x);
-      P.kb = (int)(d0 & ~31u);
-      P.nv = (int)(d0 & 31u) + 1;
-      P.bA = (int)__builtin_amdgcn_readfirstlane(d.y);
-      P.bB = (int)__builtin_amdgcn_readfirstlane(d.z);
-      const uint32_t mask = __builtin_amdgcn_readfirstlane(d.w);
-      P.in = row_ok && ((mask >> m) & 1u);
-      return true;
-    };
-    // K rows straight into the A operand (lane: key c32 of the pass); V as 4 keys x 8 dims.
-    // Interior passes (both blocks present, all 32 keys hold data) take an unconditional path.
-    auto issue = [&](const Pass& P, u32x4 (&kf)[KS], u32x4 (&vr)[VG][4]) {
-      if (P.bA >= 0 && P.bB >= 0 && P.nv == kTile) {
-        const int blk = c32 < 16 ? P.bA : P.bB;
-        const uint16_t* kp = a.k + ((size_t)blk * Hkv + g) * head_stride + (size_t)(c32 & 15) * D + 8 * h32;
+          for (int j = 0; j < VG; ++j) {
+            const int gi = lane + 64 * j, dc = gi % DC, kg = gi / DC;
+            const int vb = kg < 4 ? Pp.bA : Pp.bB;
+            const uint16_t* vp = a.v + ((size_t)vb * Hkv + g) * head_stride + (size_t)(4 * (kg & 3)) * D + 8 * dc;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[ks] = ld16(kp + 16 * ks);
+            for (int e = 0; e < 4; ++e) vr[j][e] = ld16(vp + (size_t)e * D);
+          }
+          return;
+        }
+        const int blk = c32 < 16 ? Pp.bA : Pp.bB;
+        if (blk >= 0) {
+          const uint16_t* kp = a.k + ((size_t)blk * Hkv + g) * head_stride + (size_t)(c32 & 15) * D + 8 * h32;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) kf[ks] = ld16(kp + 16 * ks);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) kf[ks] = u32x4{0, 0, 0, 0};
+        }
 #pragma unroll
         for (int j = 0; j < VG; ++j) {
           const int gi = lane + 64 * j, dc = gi % DC, kg = gi / DC;
-          const int vb = kg < 4 ? P.bA : P.bB;
-          const uint16_t* vp = a.v + ((size_t)vb * Hkv + g) * head_stride + (size_t)(4 * (kg & 3)) * D + 8 * dc;
+          const int vb = kg < 4 ? Pp.bA : Pp.bB;
+          if (vb >= 0) {
+            const uint16_t* vp = a.v + ((size_t)vb * Hkv + g) * head_stride + (size_t)(4 * (kg & 3)) * D + 8 * dc;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vr[j][e] = ld16(vp + (size_t)e * D);
+            for (int e = 0; e < 4; ++e)
+              vr[j][e] = (4 * kg + e < Pp.nv) ? ld16(vp + (size_t)e * D) : u32x4{0, 0, 0, 0};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vr[j][e] = u32x4{0, 0, 0, 0};
+          }
         }
-        return;
-      }
-      const int blk = c32 < 16 ? P.bA : P.bB;
-      if (blk >= 0) {
-        const uint16_t* kp = a.k + ((size_t)blk * Hkv + g) * head_stride + (size_t)(c32 & 15) * D + 8 * h32;
+      };
+      Pass nxt;
+      u32x4 kfA[KS], kfB[KS], vr_n[VG][4];
+      // One pass with its K in kf; the next pass is issued into kf_o (ping-pong) and vr_n.
+      auto process = [&](u32x4 (&kf)[KS], u32x4 (&kf_o)[KS]) -> bool {
+        const Pass cur = nxt;
+        // The two waves of a SIMD share its issue slots and the older one wins ties, so
+        // with equal work the younger one would finish long after (measured: a 92 us
+        // spread of 380).  A wave behind its workgroup's average progress (its LDS
+        // counter against everyone's; a stale read only delays the decision) takes the
+        // higher issue priority until it has caught up.
+        {
+          ++done;
+          if (lane == 0) prog[wave] = done;
+          int sum = 0;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[ks] = ld16(kp + 16 * ks);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[ks] = u32x4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int j = 0; j < VG; ++j) {
-        const int gi = lane + 64 * j, dc = gi % DC, kg = gi / DC;
-        const int vb = kg < 4 ? P.bA : P.bB;
-        if (vb >= 0) {
-          const uint16_t* vp = a.v + ((size_t)vb * Hkv + g) * head_stride + (size_t)(4 * (kg & 3)) * D + 8 * dc;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            vr[j][e] = (4 * kg + e < P.nv) ? ld16(vp + (size_t)e * D) : u32x4{0, 0, 0, 0};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vr[j][e] = u32x4{0, 0, 0, 0};
+          for (int i = 0; i < kWaves; ++i) sum += prog[i];
+          if (__builtin_amdgcn_readfirstlane(done * kWaves < sum)) __builtin_amdgcn_s_setprio(2);
+          else __builtin_amdgcn_s_setprio(0);
         }
+        // ---- V (bf16) -> LDS row-major; frees the V registers for the next pass
+#pragma unroll
+        for (int j = 0; j < VG; ++j) {
+          const int gi = lane + 64 * j, dc = gi % DC, kg = gi / DC;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st16(vs + (4 * kg + e) * Sm::kVStride + 8 * dc, vr_n[j][e]);
+        }
+        // the next pass's loads are in flight while this one is computed
+        const bool more = next_pass(nxt);
+        if (more) issue(nxt, kf_o, vr_n);
+        // ---- S^T = K Q^T (Q^T fragments from the wave's LDS slice)
+        f32x16 sacc = mfma32x32x16(kf[0], *reinterpret_cast<const u32x4*>(qrow), f32x16{});
+#pragma unroll
+        for (int ks = 1; ks < KS; ++ks)
+          sacc = mfma32x32x16(kf[ks], *reinterpret_cast<const u32x4*>(qrow + 16 * ks), sacc);
+        // ---- mask + online softmax (log2 domain); lane = one row, 16 keys
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = cur.kb + 8 * (i >> 2) + 4 * h32 + (i & 3);
+          const float v = (cur.in && key <= pos) ? sacc[i] * a.scale_log2 : -INFINITY;
+          sacc[i] = v;
+          mx = fmaxf(mx, v);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        // rescale only when some row's running max moved (exact: alpha = 1 otherwise)
+        if (__ballot(m_new > m_run) != 0) {
+          const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+          m_run = m_new;
+        }
+        float rs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = m_run == -INFINITY ? 0.f : fast_exp2(sacc[i] - m_run);
+          sacc[i] = p;
+          rs += p;
+        }
+        l_run += rs;
+        // the V slice written above is read back by this wave only
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          // P = P_hi + P_lo, both bf16: the pair carries ~16 significant bits of P
+          u32x4 ph, pl;
+#pragma unroll
+          for (int wv = 0; wv < 4; ++wv) {
+            const float a0 = sacc[8 * ks + 2 * wv], a1 = sacc[8 * ks + 2 * wv + 1];
+            const uint32_t hv = pack_bf16x2(a0, a1);
+            ph[wv] = hv;
+            pl[wv] = pack_bf16x2(a0 - __uint_as_float(hv << 16), a1 - __uint_as_float(hv & 0xffff0000u));
+          }
+          // this lane's keys: kbase + 0..3 and kbase + 8..11 (the P^T register order)
+          const int kbase = 16 * ks + 4 * h32;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const uint16_t* vp = vs + (kbase + (m16 >> 2)) * Sm::kVStride + 32 * mt + 16 * gq + 4 * (m16 & 3);
+            const u32x2 lo2 = lds_read_tr16(vp);
+            const u32x2 hi2 = lds_read_tr16(vp + 8 * Sm::kVStride);
+            const u32x4 va = u32x4{lo2.x, lo2.y, hi2.x, hi2.y};
+            acc[mt] = mfma32x32x16(va, ph, acc[mt]);
+            acc[mt] = mfma32x32x16(va, pl, acc[mt]);
+          }
+        }
+        // the LDS slice is rewritten by the next pass only after these reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        return more;
+      };
+      bool have = next_pass(nxt);
+      if (have) issue(nxt, kfA, vr_n);
+      // ---- this head's 32 query rows -> the wave's Q slice (read back as Q^T fragments,
+      // B operand: lane = row c32); rows of members that do not exist are zero.  Loaded
+      // after the first pass's K and V are on their way, so the two latencies overlap.
+      for (int c = lane; c < 32 * DC; c += 64) {
+        const int qr = c / DC, dc = c % DC;
+        const int mr = qr / R, rr2 = qr % R, sr = grp * M + mr;
+        u32x4 v = {0, 0, 0, 0};
+        if (mr < M && sr < a.num_seqs)
+          v = ld16(a.q + ((size_t)(sr * T + rr2 / G) * Hq + g * G + rr2 % G) * D + 8 * dc);
+        st16(qs + qr * Sm::kQStride + 8 * dc, v);
       }
-    };
-    const int m16 = lane & 15, gq = (lane >> 4) & 1;
-    Pass nxt;
-    u32x4 kfA[KS], kfB[KS], vr_n[VG][4];
-    // One pass with its K in kf; the next pass is issued into kf_o (ping-pong) and vr_n.
-    auto process = [&](u32x4 (&kf)[KS], u32x4 (&kf_o)[KS]) -> bool {
-      const Pass cur = nxt;
-      // ---- V (bf16) -> LDS row-major; frees the V registers for the next pass
-#pragma unroll
-      for (int j = 0; j < VG; ++j) {
-        const int gi = lane + 64 * j, dc = gi % DC, kg = gi / DC;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st16(vs + (4 * kg + e) * Sm::kVStride + 8 * dc, vr_n[j][e]);
-      }
-      // the next pass's loads are in flight while this one is computed
-      const bool more = next_pass(nxt);
-      if (more) issue(nxt, kf_o, vr_n);
-      // ---- S^T = K Q^T (Q^T fragments from LDS)
-      const uint16_t* qp = sm.q + c32 * Sm::kQStride + 8 * h32;
-      f32x16 sacc = mfma32x32x16(kf[0], *reinterpret_cast<const u32x4*>(qp), f32x16{});
-#pragma unroll
-      for (int ks = 1; ks < KS; ++ks)
-        sacc = mfma32x32x16(kf[ks], *reinterpret_cast<const u32x4*>(qp + 16 * ks), sacc);
-      // ---- mask + online softmax (log2 domain); lane = one row, 16 keys
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = cur.kb + 8 * (i >> 2) + 4 * h32 + (i & 3);
-        const float v = (cur.in && key <= pos) ? sacc[i] * a.scale_log2 : -INFINITY;
-        sacc[i] = v;
-        mx = fmaxf(mx, v);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      // rescale only when some row's running max moved (exact: alpha = 1 otherwise)
-      if (__ballot(m_new > m_run) != 0) {
-        const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
-        m_run = m_new;
-      }
-      float rs = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = m_run == -INFINITY ? 0.f : fast_exp2(sacc[i] - m_run);
-        sacc[i] = p;
-        rs += p;
-      }
-      l_run += rs;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        // P = P_hi + P_lo, both bf16: the pair carries ~16 significant bits of P
-        u32x4 ph, pl;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float a0 = sacc[8 * ks + 2 * w], a1 = sacc[8 * ks + 2 * w + 1];
-          const uint32_t hv = pack_bf16x2(a0, a1);
-          ph[w] = hv;
-          pl[w] = pack_bf16x2(a0 - __uint_as_float(hv << 16), a1 - __uint_as_float(hv & 0xffff0000u));
-        }
-        // this lane's keys: kbase + 0..3 and kbase + 8..11 (the P^T register order)
-        const int kbase = 16 * ks + 4 * h32;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const uint16_t* vp = vs + (kbase + (m16 >> 2)) * Sm::kVStride + 32 * mt + 16 * gq + 4 * (m16 & 3);
-          const u32x2 lo = lds_read_tr16(vp);
-          const u32x2 hi = lds_read_tr16(vp + 8 * Sm::kVStride);
-          const u32x4 va = u32x4{lo.x, lo.y, hi.x, hi.y};
-          acc[mt] = mfma32x32x16(va, ph, acc[mt]);
-          acc[mt] = mfma32x32x16(va, pl, acc[mt]);
-        }
+      while (have) {
+        have = process(kfA, kfB);
+        if (!have) break;
+        have = process(kfB, kfA);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      return more;
-    };
-    bool have = next_pass(nxt);
-    if (have) issue(nxt, kfA, vr_n);
-    while (have) {
-      have = process(kfA, kfB);
-      if (!have) break;
-      have = process(kfB, kfA);
-    }
 
-    // ---- merge the 4 wave states pairwise in a fixed order: (w0+w2) + (w1+w3)
-    l_run += __shfl_xor(l_run, 32);
-    // [2 slots][32 rows][D + 4] floats: the 16-byte row pad puts the 32 rows of one 16-byte
-  // column in distinct LDS banks
-  float* buf = reinterpret_cast<float*>(&sm.v[0][0]);
-  static_assert(kWaves / 2 * 32 * (D + 4) * 4 <= sizeof(sm.v), "merge slots fit in the V slices");
-    auto put = [&](int slot) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<f32x4*>(buf + ((size_t)slot * 32 + c32) * (D + 4) + 32 * mt + 8 * q4 + 4 * h32) =
-              f32x4{acc[mt][4 * q4], acc[mt][4 * q4 + 1], acc[mt][4 * q4 + 2], acc[mt][4 * q4 + 3]};
-      if (h32 == 0) { mrg_ml[slot][0][c32] = m_run; mrg_ml[slot][1][c32] = l_run; }
-    };
-    auto take = [&](int slot) {
-      const float mo = mrg_ml[slot][0][c32], lo = mrg_ml[slot][1][c32];
-      const float Mx = fmaxf(m_run, mo);
-      const float sa = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - Mx);
-      const float sb = (mo == -INFINITY) ? 0.f : fast_exp2(mo - Mx);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 o = *reinterpret_cast<const f32x4*>(buf + ((size_t)slot * 32 + c32) * (D + 4) + 32 * mt + 8 * q4 + 4 * h32);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][4 * q4 + i] = acc[mt][4 * q4 + i] * sa + o[i] * sb;
-        }
-      l_run = l_run * sa + lo * sb;
-      m_run = Mx;
-    };
-    // tree: waves [h, 2h) hand their state to waves [0, h), h = kWaves/2 .. 1
-#pragma unroll
-    for (int h = kWaves / 2; h >= 1; h /= 2) {
-      __syncthreads();
-      if (wave >= h && wave < 2 * h) put(wave - h);
-      __syncthreads();
-      if (wave < h) take(wave);
-    }
-    if (wave == 0) {
-      // every row is written (rows of members outside the unit get lse = -inf); the
-      // combine reads only the rows of real sequences
-      const size_t pidx = (size_t)item * 32 + c32;
-      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+      // ---- the piece's partial: every row is written (rows of members that do not exist
+      // get lse = -inf); the combine reads only the rows of real sequences
+      const float l_tot = l_run + __shfl_xor(l_run, 32);
+      const size_t pidx = (((size_t)piece * NS + sub) * Hkv + g) * 32 + c32;
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       float* op = a.part_o + pidx * D;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -475,13 +495,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int q4 = 0; q4 < 4; ++q4)
           *reinterpret_cast<f32x4*>(op + 32 * mt + 8 * q4 + 4 * h32) =
               f32x4{acc[mt][4 * q4] * inv, acc[mt][4 * q4 + 1] * inv, acc[mt][4 * q4 + 2] * inv, acc[mt][4 * q4 + 3] * inv};
-      if (h32 == 0) a.part_lse[pidx] = l_run > 0.f ? m_run + __log2f(l_run) : -INFINITY;
-    }
-  }  // work items
+      if (h32 == 0) a.part_lse[pidx] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
+      // the Q slice is rewritten for the next head or piece only after this wave's reads
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }  // heads of this wave
+  }  // regions
 }
 
-// Resident workgroups of the persistent decode grid: 8 / kWaves per compute unit.
-int decode_grid(int units_cap, int num_kv_heads) {
+}  // namespace
+
+int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -490,27 +515,23 @@ int decode_grid(int units_cap, int num_kv_heads) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
     cus[dev] = n;
   }
-  const long items = (long)units_cap * num_kv_heads;
-  return (int)std::min<long>(items, (long)(8 / kWaves) * cus[dev]);
+  return cus[dev];
 }
-
-}  // namespace
 
 hipError_t launch_gqa_decode_plan(const GqaDecodeArgs& a, hipStream_t stream) {
   const unsigned regions = (unsigned)a.dims.n_groups * a.dims.n_chunks;
   if (regions == 0) return hipSuccess;
   hipLaunchKernelGGL(decode_plan_kernel, dim3(regions), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(decode_units_kernel, dim3(1), dim3(1024), 0, stream, a);
+  hipLaunchKernelGGL(decode_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gqa_decode(const GqaDecodeArgs& a, hipStream_t stream) {
   if (a.dims.n_groups == 0 || a.dims.n_chunks == 0) return hipSuccess;
-  const int grid = decode_grid(a.dims.units_cap, a.num_kv_heads);
   if (a.head_dim == 128)
-    hipLaunchKernelGGL((gqa_decode_kernel<128>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((gqa_decode_kernel<128>), dim3(a.dims.grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((gqa_decode_kernel<64>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((gqa_decode_kernel<64>), dim3(a.dims.grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -545,13 +566,15 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     base = ((size_t)seq * a.pf_max_new + j) * a.max_splits * a.rows + row;   // token slot
     s = a.pf_q_start[seq] + j;                                                // output row
     stride = a.rows;
-  } else if (a.unit_start != nullptr) {
+  } else if (a.piece_start != nullptr) {
+    // GQA decode: the group's pieces are consecutive, each with `subs` sub-range partials,
+    // in pass order; slot ((piece * subs + sub) * Hkv + head), row m * R + t * G + hq % G
     const int Hq = a.rows / a.q_per_seq, G = Hq / a.num_kv_heads, R = a.q_per_seq * G;
     const int t = row / Hq, hq = row % Hq, head = hq / G;
     const int g = s / a.members, m = s % a.members;
-    const int u0 = a.unit_start[g * a.n_chunks], u1 = a.unit_start[(g + 1) * a.n_chunks];
-    n = u1 - u0;
-    base = ((size_t)u0 * a.num_kv_heads + head) * 32 + m * R + t * G + hq % G;
+    const int u0 = a.piece_start[g * a.n_chunks], u1 = a.piece_start[(g + 1) * a.n_chunks];
+    n = (u1 - u0) * a.subs;
+    base = ((size_t)u0 * a.subs * a.num_kv_heads + head) * 32 + m * R + t * G + hq % G;
     stride = (long)a.num_kv_heads * 32;
   } else {
     const int L = min(max(a.context_len[s], 0), a.max_context_len);

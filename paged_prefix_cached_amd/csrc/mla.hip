@@ -56,47 +56,6 @@ static_assert(kKS >= kDqk + 16, "row 0's padding takes the discarded chunk slots
 template <int N>
 using Int = std::integral_constant<int, N>;
 
-// LDS-DMA of 16 (or 4) bytes per lane: lane l's global bytes land at LDS byte address
-// lds_dst + 16 l (4 l); lds_dst must be the same for every lane.  Issued as inline assembly, so the compiler
-// does not track these LDS writes: it would otherwise wait for every outstanding DMA
-// before any LDS read it cannot prove disjoint (the S exchange and the transpose reads
-// among them), draining the pipeline.  The pipeline waits explicitly (wait_vm0, then a
-// barrier) before any wave reads what a DMA wrote.  M0 holds the LDS base; nothing else
-// in these kernels uses M0.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_dst) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane(lds_dst);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(l) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* src, uint32_t lds_dst) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane(lds_dst);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(l) : "memory", "m0");
-}
-// LDS byte address of a pointer into a __shared__ object.
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-#pragma clang diagnostic pop
-// Wait until no vector-memory operation of this wave is outstanding (gfx9 s_waitcnt
-// encoding: vmcnt 0, expcnt and lgkmcnt left at their maxima).
-// (also a compiler barrier: no LDS read of DMA data moves above it)
-__device__ __forceinline__ void wait_vm0() {
-  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-  asm volatile("" ::: "memory");
-}
-// Workgroup barrier that orders LDS accesses only.  A full __syncthreads() also waits for
-// outstanding vector-memory operations -- here the LDS-DMA of a later tile, still in
-// flight on purpose.
-// (An LDS-scoped fence is no help: LDS-DMA writes count as LDS writes, so it waits for
-// them too.)  The compiler-level memory clobbers keep LDS accesses on their side of it.
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt left at their maxima
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // NW waves per workgroup; SPLIT waves share each group of 32 query rows (1: a wave holds
 // all 576 Q dims and all 512 output dims; 2 or 4: the waves split both, exchanging
 // partial S through LDS).  STAGED (sparse only): the physical rows of the selections

@@ -145,15 +145,13 @@ hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
 
 // ---- decode workspace layouts
 // MLA: partial outputs [S][max_splits][rows][512] then partial log2-sum-exp.
-// GQA: unit partials, partial log2-sum-exp, the pass lists, pass counts, unit starts,
-// the unit table and the work queue (each part 256-byte aligned).
+// GQA: piece partials, partial log2-sum-exp, the pass lists, pass counts, region starts
+// and piece starts (each part 256-byte aligned).
 struct DecodeLayout {
   int max_splits, rows, d_v, split;
   pa::GqaDecodeDims dims;
-  size_t o_bytes, lse_bytes, pass_bytes, npass_bytes, ustart_bytes, unit_bytes, queue_bytes;
-  size_t total() const {
-    return o_bytes + lse_bytes + pass_bytes + npass_bytes + ustart_bytes + unit_bytes + queue_bytes;
-  }
+  size_t o_bytes, lse_bytes, pass_bytes, npass_bytes, rstart_bytes, pstart_bytes;
+  size_t total() const { return o_bytes + lse_bytes + pass_bytes + npass_bytes + rstart_bytes + pstart_bytes; }
 };
 
 DecodeLayout decode_layout(int num_seqs, int q_per_seq, int num_q_heads, int max_context_len,
@@ -171,14 +169,13 @@ DecodeLayout decode_layout(int num_seqs, int q_per_seq, int num_q_heads, int max
   const int hkv = pool->num_kv_heads;
   l.dims = pa::gqa_decode_dims(num_seqs, q_per_seq, num_q_heads, hkv, max_context_len);
   const size_t regions = (size_t)l.dims.n_groups * l.dims.n_chunks;
-  const size_t slots = (size_t)l.dims.units_cap * hkv * 32;
+  const size_t slots = (size_t)l.dims.pieces_cap * l.dims.subs * hkv * 32;
   l.o_bytes = round_up(slots * l.d_v * sizeof(float), 256);
   l.lse_bytes = round_up(slots * sizeof(float), 256);
   l.pass_bytes = round_up(regions * l.dims.region_cap * 16, 256);
   l.npass_bytes = round_up(regions * sizeof(int32_t), 256);
-  l.ustart_bytes = round_up((regions + 1) * sizeof(int32_t), 256);
-  l.unit_bytes = round_up((size_t)l.dims.units_cap * 16, 256);
-  l.queue_bytes = 256;
+  l.rstart_bytes = round_up((regions + 1) * sizeof(int32_t), 256);
+  l.pstart_bytes = round_up((regions + 1) * sizeof(int32_t), 256);
   return l;
 }
 
@@ -363,11 +360,9 @@ static pa_status decode_impl(const void* q, const pa_kv_pool* pool, const int32_
     off += l.pass_bytes;
     a.n_passes = reinterpret_cast<int32_t*>(ws + off);
     off += l.npass_bytes;
-    a.unit_start = reinterpret_cast<int32_t*>(ws + off);
-    off += l.ustart_bytes;
-    a.units = reinterpret_cast<uint32_t*>(ws + off);
-    off += l.unit_bytes;
-    a.queue = reinterpret_cast<int32_t*>(ws + off);
+    a.region_start = reinterpret_cast<int32_t*>(ws + off);
+    off += l.rstart_bytes;
+    a.piece_start = reinterpret_cast<int32_t*>(ws + off);
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(pool->k);
     a.v = static_cast<const uint16_t*>(pool->v);
@@ -387,7 +382,8 @@ static pa_status decode_impl(const void* q, const pa_kv_pool* pool, const int32_
     a.scale_log2 = scale * 1.4426950408889634f;
     PA_TRY(launched(timed("decode_plan", stream, [&] { return pa::launch_gqa_decode_plan(a, stream); }), "decode plan launch"));
     PA_TRY(launched(timed("decode_gqa", stream, [&] { return pa::launch_gqa_decode(a, stream); }), "decode launch"));
-    c.unit_start = a.unit_start;
+    c.piece_start = a.piece_start;
+    c.subs = l.dims.subs;
     c.members = l.dims.members;
     c.n_chunks = l.dims.n_chunks;
     c.num_kv_heads = pool->num_kv_heads;

@@ -155,6 +155,47 @@ __device__ __forceinline__ int32_t xcd_unit_swizzle(int32_t hw_id, int32_t n, in
   return ((k / per_unit) * 8 + (hw_id & 7)) * per_unit + k % per_unit;
 }
 
+// LDS-DMA of 16 (or 4) bytes per lane: lane l's global bytes land at LDS byte address
+// lds_dst + 16 l (4 l); lds_dst must be the same for every lane.  Issued as inline assembly, so the compiler
+// does not track these LDS writes: it would otherwise wait for every outstanding DMA
+// before any LDS read it cannot prove disjoint (the S exchange and the transpose reads
+// among them), draining the pipeline.  The pipeline waits explicitly (wait_vm0, then a
+// barrier) before any wave reads what a DMA wrote.  M0 holds the LDS base; nothing else
+// in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_dst) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(l) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds_dst) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(l) : "memory", "m0");
+}
+// LDS byte address of a pointer into a __shared__ object.
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+#pragma clang diagnostic pop
+// Wait until no vector-memory operation of this wave is outstanding (gfx9 s_waitcnt
+// encoding: vmcnt 0, expcnt and lgkmcnt left at their maxima).
+// (also a compiler barrier: no LDS read of DMA data moves above it)
+__device__ __forceinline__ void wait_vm0() {
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+// Workgroup barrier that orders LDS accesses only.  A full __syncthreads() also waits for
+// outstanding vector-memory operations -- here the LDS-DMA of a later tile, still in
+// flight on purpose.
+// (An LDS-scoped fence is no help: LDS-DMA writes count as LDS writes, so it waits for
+// them too.)  The compiler-level memory clobbers keep LDS accesses on their side of it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float wave_max_xor(float v, int lanes) {
   for (int o = lanes >> 1; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;

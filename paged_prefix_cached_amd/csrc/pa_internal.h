@@ -13,25 +13,22 @@ namespace pa {
 #endif
 constexpr int kDecodeSplitMla = PA_DECODE_SPLIT_MLA;
 
-// GQA decode work units: a group's list of distinct block-pair passes is cut into units
-// of at most kUnitPasses passes (one partial (o, lse) per unit and KV head); the plan
-// covers kPlanTiles 32-key tiles per workgroup.
-#ifndef PA_DECODE_WAVES
-#define PA_DECODE_WAVES 8
-#endif
-#ifndef PA_DECODE_UNIT_PASSES
-#define PA_DECODE_UNIT_PASSES (16 * PA_DECODE_WAVES)
-#endif
-constexpr int kUnitPasses = PA_DECODE_UNIT_PASSES;
+// GQA decode: the plan covers kPlanTiles 32-key tiles of a group per workgroup (a region).
 constexpr int kPlanTiles = 256;
+
+// Compute units of the current device (read once per device): the GQA decode grid and the
+// prefill split decision depend on it, so workspace queries and calls agree.
+int device_cus();
 
 // Host-side sizes of the GQA decode workspace (shared by the C ABI and the launcher).
 struct GqaDecodeDims {
   int32_t members;      // sequences per group: 32 / (q_per_seq * group size), >= 1
   int32_t n_groups;     // ceil(num_seqs / members)
-  int32_t n_chunks;     // plan chunks per group: ceil(ceil(max_context_len / 32) / kPlanTiles)
+  int32_t n_chunks;     // plan regions per group: ceil(ceil(max_context_len / 32) / kPlanTiles)
   int32_t region_cap;   // pass capacity of one (group, chunk) region: kPlanTiles * members
-  int32_t units_cap;    // upper bound of units over all groups
+  int32_t grid;         // attention workgroups: one per compute unit
+  int32_t subs;         // sub-ranges per (piece, KV head): 8 / Hkv when Hkv divides 8, else 1
+  int32_t pieces_cap;   // upper bound of pieces: regions + grid - 1
 };
 GqaDecodeDims gqa_decode_dims(int num_seqs, int q_per_seq, int num_q_heads, int num_kv_heads,
                               int max_context_len);
@@ -68,14 +65,15 @@ struct GqaDecodeArgs {
   const uint16_t* v;
   const int32_t* bt;
   const int32_t* context_len;
-  float* part_o;        // [units_cap * Hkv * 32][D]: unit u, KV head h, tile row r at (u*Hkv+h)*32+r
-  float* part_lse;      // [units_cap * Hkv * 32], log2 units
+  float* part_o;        // [pieces_cap * subs * Hkv * 32][D]: piece p, sub-range b, KV head h,
+                        //   tile row r at ((p * subs + b) * Hkv + h) * 32 + r
+  float* part_lse;      // [pieces_cap * subs * Hkv * 32], log2 units
   uint32_t* passes;     // [n_groups * n_chunks][region_cap][4]: {key base | (valid keys - 1),
                         //   block A, block B, member mask}
   int32_t* n_passes;    // [n_groups * n_chunks]
-  int32_t* unit_start;  // [n_groups * n_chunks + 1]: first unit of each region; total last
-  uint32_t* units;      // [units_cap][4]: {group, first pass, end pass, 0} (pass indices absolute)
-  int32_t* queue;       // [2]: next work item, number of items (units * Hkv)
+  int32_t* region_start;  // [n_groups * n_chunks + 1]: compact index of each region's first
+                          //   pass; the total last
+  int32_t* piece_start;   // [n_groups * n_chunks + 1]: first piece of each region; total last
   int32_t bt_stride, num_seqs, q_per_seq, num_q_heads, num_kv_heads, head_dim, num_blocks;
   int32_t max_context_len;
   GqaDecodeDims dims;
@@ -89,10 +87,11 @@ struct CombineArgs {
   uint16_t* out;                // [S][rows][D]
   float* lse;                   // [S][rows] or null
   int32_t num_seqs, rows, head_dim, max_splits, split, max_context_len;
-  // GQA unit partials (unit_start != null): row (t, hq) of sequence s reads the units of
-  // its group; otherwise partials are [S][max_splits][rows] with split `split`.
-  const int32_t* unit_start;
-  int32_t members, n_chunks, num_kv_heads, q_per_seq;
+  // GQA decode partials (piece_start != null): row (t, hq) of sequence s reads the pieces
+  // of its group (subs partials each); otherwise partials are [S][max_splits][rows] with
+  // split `split`.
+  const int32_t* piece_start;
+  int32_t members, n_chunks, num_kv_heads, q_per_seq, subs;
   // Split-K prefill partials (pf_q_start != null): workgroup (s, j, head) merges the
   // partials of new token j of sequence s, written at [s * pf_max_new + j][split][rows]
   // (rows = heads), and writes output row q_start[s] + j.
@@ -193,7 +192,7 @@ struct AppendArgs {
 };
 
 hipError_t launch_gqa_prefill(const GqaPrefillArgs& a, hipStream_t s);
-// GQA decode = plan (pass lists, units, queue reset) then the persistent attention grid.
+// GQA decode = plan (pass lists, numbering) then the attention grid of one workgroup per CU.
 hipError_t launch_gqa_decode_plan(const GqaDecodeArgs& a, hipStream_t s);
 hipError_t launch_gqa_decode(const GqaDecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);

@@ -337,18 +337,11 @@ hipError_t launch_d(const GqaPrefillArgs& a, int G, unsigned grid, hipStream_t s
 constexpr int kPrefillSplitLen = PA_PREFILL_SPLIT_LEN;
 int prefill_split_len(int num_seqs, int num_q_heads, int num_kv_heads, int max_new_len, int max_total_len) {
   if (num_seqs <= 0 || num_kv_heads <= 0 || max_new_len <= 0) return 0;
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
+  const int cus = device_cus();
   const int G = num_q_heads / num_kv_heads;
   const int TT = kRows / (G > 0 ? G : 1);
   const long wgs = (long)((max_new_len + TT - 1) / TT) * num_kv_heads * num_seqs;
-  if (wgs >= 4L * cus[dev] || max_total_len <= 2 * kPrefillSplitLen) return 0;
+  if (wgs >= 4L * cus || max_total_len <= 2 * kPrefillSplitLen) return 0;
   return kPrefillSplitLen;
 }
 
