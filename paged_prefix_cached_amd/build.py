@@ -19,8 +19,10 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpa.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["pa_abi.cpp", "gather.hip", "prefill_gqa.hip", "decode_gqa.hip", "mla.hip",
+SOURCES = ["pa_abi.cpp", "gather.hip", "prefill_gqa.hip", "decode_gqa.hip", "mla.hip", "mla_exact.hip",
            "indexer.hip", "topk.hip", "append.hip"]
+# Per-source flags (none at present).
+EXTRA = {}
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}", "-Wall",
@@ -34,7 +36,7 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -196,8 +196,11 @@ hipError_t launch_gqa_prefill(const GqaPrefillArgs& a, hipStream_t s);
 hipError_t launch_gqa_decode_plan(const GqaDecodeArgs& a, hipStream_t s);
 hipError_t launch_gqa_decode(const GqaDecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+// MLA: the fixed-reference kernel, then the exact kernel over the units it marked
 hipError_t launch_mla_decode(const MlaDecodeArgs& a, hipStream_t s);
 hipError_t launch_sparse_mla(const SparseMlaArgs& a, hipStream_t s);
+hipError_t launch_mla_decode_exact(const MlaDecodeArgs& a, hipStream_t s);
+hipError_t launch_sparse_mla_exact(const SparseMlaArgs& a, hipStream_t s);
 hipError_t launch_indexer_scores(const IndexerArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
