@@ -16,7 +16,8 @@
 //
 // Keys go in 32-key tiles through an NBUF-deep LDS-DMA pipeline (global_load_lds, 16 bytes
 // a lane, no registers held while the loads fly): tile t + NBUF - 1 is gathered while tile
-// t is computed, one barrier per tile.  The tile stays FP8 in LDS, chunk-major: 16-byte
+// t is computed -- its row loads spread over the Q.K pass rather than issued in one burst --
+// with one barrier per tile.  The tile stays FP8 in LDS, chunk-major: 16-byte
 // chunk c of key r sits at c * 512 + 16 (r ^ 4 (c & 1)).  So a DMA lane fetches the same
 // key for every chunk pair it loads (one row address per lane and tile), the Q.K fragment
 // reads of a k-step cover 512 contiguous bytes, and the transposed V reads of a half-wave
@@ -59,8 +60,9 @@ constexpr int kSelLds = 2048;                // sparse selections staged in LDS
 constexpr float kSlack = 8.f;                // log2 units: probabilities stay <= 2^8
 constexpr int kPre = 8;                      // LDS fragment reads in flight ahead of use
 
-// Source of the DMA for keys that are not to be read: a latent row and a scale of zeros.
-__device__ __attribute__((aligned(16))) uint8_t kZeroRow[kDqk] = {};
+// Source of the DMA for keys that are not to be read (a latent row and a scale of zeros) and
+// of the filler loads that keep every wave's DMA count equal: 1 KB of zeros.
+__device__ __attribute__((aligned(16))) uint8_t kZeroRow[1024] = {};
 
 // Eight FP8 (E4M3) bytes -> eight fp16 (exact), as an MFMA operand.
 __device__ __forceinline__ u32x4 fp8x8_to_f16x8(u32x2 b) {
@@ -111,6 +113,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   __shared__ __attribute__((aligned(16))) float tsc[NBUF][kKT];     // per-key scale (0 if invalid)
   __shared__ uint32_t tmask[NBUF];                                  // bit k: key k is valid
   __shared__ int32_t ovf_s[NW];                                     // per wave: a row overflowed
+  constexpr bool kFiller = NW * kLoadsMax != kTileLoads;           // some waves have a spare load
+  __shared__ __attribute__((aligned(16))) uint8_t spare[kFiller ? 1024 : 16];  // its target
   __shared__ int32_t bt_s[SPARSE ? 1 : kDecodeSplitMla / kBs + 1];
   __shared__ int32_t sel_s[SPARSE && STAGED ? kSelLds : 1];
 
@@ -217,7 +221,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   asm volatile("" : "+s"(zero));                      // one address, kept in scalar registers
   const int dma_key = l32 ^ (4 * h);
   const int dma_col = 32 * wave + 16 * h;
-  auto issue = [&](int B, int tt) {
+  // Per tile: prep() resolves the lane's row (tt >= n_tiles: the zero row, so that every
+  // step issues the same number of DMA instructions), issues the scale load and writes the
+  // valid mask; the kLoadsMax row loads are spread over the next Q.K pass (load()).
+  struct Dma {
+    const uint8_t* rowp;
+    uint32_t dst;
+  };
+  auto prep = [&](int B, int tt) -> Dma {
     const int kb = tt * kKT;
     const uint32_t dst = lds_u32(&raw[B][0]) + 1024 * wave;
     const uint8_t* rowp;                               // this lane's key row (or zeros)
@@ -236,17 +247,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
       sclp = valid ? ksb + (qb >> 6) * (size_t)sblk_bytes + 4 * (qb & (kBs - 1)) : zero;
     } else {
       const int pos0 = k_begin + kb;
-      const int pb = __builtin_amdgcn_readfirstlane(bt_s[pos0 / kBs - lb_base]);
+      const int pb = tt < n_tiles ? __builtin_amdgcn_readfirstlane(bt_s[pos0 / kBs - lb_base]) : -1;
       valid = pb >= 0 && kb + dma_key < n_keys;
       const size_t o = (size_t)(pos0 % kBs + dma_key);
       rowp = valid ? kv + (size_t)max(pb, 0) * (size_t)blk_bytes + o * kDqk : zero;
       sclp = valid ? ksb + (size_t)max(pb, 0) * (size_t)sblk_bytes + 4 * o : zero;
-    }
-    rowp += dma_col;
-#pragma unroll
-    for (int m = 0; m < kLoadsMax; ++m) {
-      if (wave + NW * m >= kTileLoads) break;
-      dma16(rowp + 32 * NW * m, dst + 1024 * NW * m);
     }
     // lanes 0-31 hold keys 0-31 (h = 0: dma_key = lane): the scales and the valid mask
     const uint32_t vmask = (uint32_t)__ballot(h == 0 && valid);
@@ -254,9 +259,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
       if (h == 0) dma4(sclp, lds_u32(&tsc[B][0]));
       if (lane == 0) tmask[B] = vmask;
     }
+    return Dma{rowp + dma_col, dst};
+  };
+  // Load m of the tile; a wave with fewer loads than kLoadsMax issues a filler load of
+  // zeros into `spare` instead (no branch inside the Q.K pass, same count on every wave).
+  auto load = [&](const Dma& d, int m) {
+    if constexpr (kFiller) {
+      const bool real = wave + NW * m < kTileLoads;   // uniform
+      dma16((real ? d.rowp : zero + dma_col) + 32 * NW * m, real ? d.dst + 1024 * NW * m : lds_u32(spare));
+    } else {
+      dma16(d.rowp + 32 * NW * m, d.dst + 1024 * NW * m);
+    }
   };
   // DMA instructions this wave issues per tile (the last wave adds the scale load)
-  const int my_loads = (kTileLoads - wave + NW - 1) / NW + (wave == NW - 1 ? 1 : 0);
+  const int my_loads = kLoadsMax + (wave == NW - 1 ? 1 : 0);
 
   f32x16 acc[kMT];
   // m_run: the row's reference maximum (log2 units), set at its first valid key and fixed
@@ -287,8 +303,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   const int v_base = (vg & 1) * kColB + 16 * (v_key0 ^ (4 * (vg & 1))) + 8 * vhh;   // + 256 kk + 1024 mt
   lds_u8* const lds = (lds_u8*)&raw[0][0];
 
-  // S^T = K Q^T over the 36 k-steps of tile buffer B
-  auto qk = [&](int B) -> f32x16 {
+  // S^T = K Q^T over the 36 k-steps of tile buffer B (fragment reads kPre ahead), with the
+  // row loads of the next tile spread over the pass
+  auto qk = [&](int B, const Dma& d) -> f32x16 {
     const int tk = B * kTileB;
     f32x16 s0;
 #pragma unroll
@@ -302,10 +319,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
       const int n = i + kPre;
       if (n < kQS) kr[i % kPre] = lds_read_b64(lds, tk + n * kColB + ((n & 1) ? k_odd : k_even));
       s0 = mfma32x32x16_f16(fp8x8_to_f16x8(kc), qf[i], s0);
+      constexpr int kEvery = kQS / kLoadsMax;
+      if (i % kEvery == kEvery / 2 && i / kEvery < kLoadsMax) load(d, i / kEvery);
     }
     return s0;
   };
-  // O^T += V^T P^T over tile buffer B
+  // O^T += V^T P^T over tile buffer B (fragment reads kPre ahead)
   auto pv = [&](int B, const u32x4 (&pb)[2]) {
     const int tv = B * kTileB + v_base;
     u32x2 vr[kPre];
@@ -366,28 +385,32 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     l_run += rs;
   };
 
-  // ---- pipeline: buffer t % NBUF holds tile t; tile t + NBUF - 1 is issued at step t into
-  // the buffer tile t - 1 used, after the barrier that ends every wave's use of it
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+  // ---- pipeline: buffer t % NBUF holds tile t; tile t + NBUF - 1 is issued at step t into
+  // the buffer tile t - 1 used, after the barrier that ends every wave's use of it.  Every
+  // step issues my_loads DMA instructions (zero rows past the last tile), so before step t
+  // exactly (NBUF - 2) * my_loads of them follow tile t's.
 #pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i)
-    if (i < n_tiles) issue(i, i);
+  for (int i = 0; i < NBUF - 1; ++i) {
+    const Dma d = prep(i, i);
+#pragma unroll
+    for (int m = 0; m < kLoadsMax; ++m) load(d, m);
+  }
   for (int t = 0; t < n_tiles; ++t) {
-    // this wave's DMA of tile t has landed: the loads of up to NBUF - 2 later tiles may
-    // still be in flight
-    if constexpr (NBUF == 2) wait_vm<0>();
-    else wait_vm_upto<(NBUF - 2) * (kLoadsMax + 1)>(min(n_tiles - 1 - t, NBUF - 2) * my_loads);
+    // this wave's DMA of tile t has landed
+    wait_vm_upto<(NBUF - 2) * (kLoadsMax + 1)>((NBUF - 2) * my_loads);
     barrier_lds();
-    if (t + NBUF - 1 < n_tiles) issue((t + NBUF - 1) % NBUF, t + NBUF - 1);
     const int B = t % NBUF;
+    const Dma d = prep((t + NBUF - 1) % NBUF, t + NBUF - 1);
     u32x4 pb[2];
-    const f32x16 s0 = qk(B);
+    const f32x16 s0 = qk(B, d);
     softmax(B, t, s0, pb);
     pv(B, pb);
   }
+  wait_vm<0>();                                       // no DMA outlives the workgroup
   {
     const bool w_ovf = __ballot(ovf) != 0;
     if (lane == 0) ovf_s[wave] = w_ovf ? 1 : 0;
