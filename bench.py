@@ -110,11 +110,43 @@ def _kms(t):
     return {k: v["mean"] for k, v in t["kernels"].items()}
 
 
-def _mfma_roof(flops, k_ms, kernel, per_unit, peak=None):
+# Sustained dense-GEMM rate on this device (vendor library, random operands), measured once
+# per run: under full matrix-core load with random data the engine clock drops well below
+# its peak, so this -- not the published peak -- is the rate a kernel can actually reach.
+GEMM_CEILING = {}
+
+
+def gemm_ceiling(n=8192, reps=10):
+    """TFLOP/s of torch.matmul (hipBLASLt) on random n x n fp16 and bf16 operands."""
+    import torch
+    out = {}
+    for name, dt in (("fp16", torch.float16), ("bf16", torch.bfloat16)):
+        g = torch.Generator(device="cuda").manual_seed(7)
+        a = torch.randn(n, n, device="cuda", dtype=dt, generator=g)
+        b = torch.randn(n, n, device="cuda", dtype=dt, generator=g)
+        for _ in range(3):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        del a, b
+    return out
+
+
+def _mfma_roof(flops, k_ms, kernel, per_unit, peak=None, dtype="fp16"):
     peak = BF16_PEAK_TFLOPS if peak is None else peak
     ach = flops / (k_ms * 1e-3) / 1e12
-    return {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
-            "traffic": None, "kernel": kernel, "flop_per_launch": flops, "per_unit": per_unit}
+    r = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
+         "traffic": None, "kernel": kernel, "flop_per_launch": flops, "per_unit": per_unit}
+    if dtype in GEMM_CEILING:
+        r["sustained_gemm_tflops"] = GEMM_CEILING[dtype]
+        r["frac_of_sustained_gemm"] = ach / GEMM_CEILING[dtype]
+    return r
 
 
 def measured_traffic(counters_file: str, sources: list[str]):
@@ -295,7 +327,7 @@ def _bench_gqa_prefill_workload(wl, label, steps, warmup):
     return {"workload": label, "ms": ms, "ms_min": tm["ms_min"], "tflops": flops / (ms * 1e-3) / 1e12,
             "tokens_per_s": wl.q.shape[0] / (ms * 1e-3), "kernel_ms": _kms(tm), "flop": flops,
             "roofline": _mfma_roof(flops, _kmean(tm, "prefill_gqa"), "gqa_prefill_kernel",
-                                   "4 x 128 FLOP per (query head, visible key)")}
+                                   "4 x 128 FLOP per (query head, visible key)", dtype="bf16")}
 
 
 def bench_prefill(steps, warmup):
@@ -364,7 +396,7 @@ def bench_chunked(steps, warmup):
             "flop": flops, "decode_kv_bytes": kv_bytes,
             "decode_kv_gbps": kv_bytes / (_kmean(tm, "decode_gqa") * 1e-3) / 1e9,
             "roofline": _mfma_roof(flops, _kmean(tm, "prefill_gqa"), "gqa_prefill_kernel",
-                                   "4 x 128 FLOP per (query head, visible key)")}
+                                   "4 x 128 FLOP per (query head, visible key)", dtype="bf16")}
 
 
 def bench_mla(steps, warmup):
@@ -442,7 +474,7 @@ def bench_sparse(steps, warmup, packed=False):
     k_top = _kmean(tm, "topk")
     roofs = {
         "indexer": _mfma_roof(idx_flops, _kmean(tm, "indexer"), "indexer_kernel",
-                              "2 x 128 FLOP per (query, indexer head, visible key)"),
+                              "2 x 128 FLOP per (query, indexer head, visible key)", dtype="bf16"),
         "topk": {"bound": "hbm", "achieved": topk_bytes / (k_top * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                  "unit": "GB/s", "frac": topk_bytes / (k_top * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
                  "kernel": "topk_kernel", "bytes_per_launch": topk_bytes,
@@ -589,6 +621,9 @@ def main():
         line[k] = res[k]
     line["clocks"] = _clocks()
     if args.secondary:
+        GEMM_CEILING.update(gemm_ceiling())
+        line["sustained_gemm_tflops"] = dict(GEMM_CEILING)
+        log(f"[bench] sustained GEMM rate: {GEMM_CEILING}")
         sec = {}
         for c in [x.strip() for x in args.secondary.split(",") if x.strip()]:
             if c == "2n":   # control: the same decode batch with no shared blocks
