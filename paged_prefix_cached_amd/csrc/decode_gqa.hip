@@ -155,8 +155,26 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(GqaDecodeArgs a) {
 // an empty range (P / N >= 1).  A piece is a region's share of one workgroup's range, so
 // region r holds wg_of(last) - wg_of(first) + 1 pieces (0 when it has no pass), and the
 // pieces of a group are numbered consecutively in pass order.
-// wg_of(x): the workgroup whose range holds pass x, max{w : floor(w P / N) <= x}.
-__device__ __forceinline__ int wg_of(long x, long P, long N) { return (int)(((x + 1) * N - 1) / P); }
+// Workgroup w of N takes passes [wg_bound(w), wg_bound(w + 1)).  Workgroups go to the 8
+// XCDs round robin (XCD = w mod 8), and the odd XCDs run the same passes about 4.5 % slower
+// (per-workgroup end stamps on MI355X, repeatable launch to launch); so when every
+// workgroup has plenty of passes the even ones take kXcdSkew / 1024 more than an equal share
+// and the odd ones as much less.
+constexpr long kXcdSkew = 23;
+__device__ __forceinline__ long wg_bound(long w, long P, long N) {
+  if (P < 8 * N) return w * P / N;                  // few passes: equal shares
+  // weights 1024 +- kXcdSkew alternate, so the cumulative weight is 1024 w + kXcdSkew (w & 1)
+  return P * (1024 * w + kXcdSkew * (w & 1)) / (1024 * N + kXcdSkew * (N & 1));
+}
+// wg_of(x): the workgroup whose range holds pass x, max{w : wg_bound(w) <= x}.  The skew
+// moves a boundary by less than one share, so the equal-share estimate is off by at most one.
+__device__ __forceinline__ int wg_of(long x, long P, long N) {
+  long w = ((x + 1) * N - 1) / P;
+  w = w < 0 ? 0 : (w > N - 1 ? N - 1 : w);
+  while (w + 1 < N && wg_bound(w + 1, P, N) <= x) ++w;
+  while (w > 0 && wg_bound(w, P, N) > x) --w;
+  return (int)w;
+}
 __device__ __forceinline__ long active_wgs(long grid, long P) { return grid < P ? grid : P; }
 
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
@@ -270,7 +288,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const long N = active_wgs(gridDim.x, P);
   const int w = blockIdx.x;
   if (w >= N) return;                               // fewer passes than workgroups
-  const int lo = (int)((long)w * P / N), hi = (int)((long)(w + 1) * P / N);
+  const int lo = (int)wg_bound(w, P, N), hi = (int)wg_bound(w + 1, P, N);
   // this wave's (head, sub-range): NS = 8 / Hkv sub-ranges when Hkv divides 8, else one
   // and heads wave, wave + 8, ...
   const int sub = NS > 1 ? wave / Hkv : 0;
