@@ -233,3 +233,86 @@ def test_sparse_mla_given_selection(pa_lib, k):
     ro, _ = oracle.sparse_mla_attention(mla.q[0:n], codes, sc, tk, mla.scale)
     assert_close(got, ro, FP8_MAX_ABS, FP8_L1, f"sparse given selection k={k}")
     assert np.all(got[n - 1] == 0)
+
+
+def _tile_overflow(scores_log2: np.ndarray, tile: int = 32, slack: float = 8.0) -> np.ndarray:
+    """Per row of scores (log2 units, -inf = masked, in the kernel's key order): whether the
+    MLA kernel's fixed reference (the row maximum of the first tile holding a visible key)
+    is passed by more than `slack` by a later tile's maximum -- the case the kernel hands to
+    its exact fallback."""
+    n, L = scores_log2.shape
+    pad = (-L) % tile
+    s = np.concatenate([scores_log2, np.full((n, pad), -np.inf)], axis=1).reshape(n, -1, tile).max(axis=2)
+    out = np.zeros(n, dtype=bool)
+    for r in range(n):
+        fin = np.flatnonzero(np.isfinite(s[r]))
+        if fin.size:
+            out[r] = bool(np.max(s[r][fin[0]:]) > s[r][fin[0]] + slack)
+    return out
+
+
+def test_mla_decode_fixed_reference_fallback(pa_lib):
+    """Moderately peaked queries: in some work units (4,096 keys x 128 query rows) a row's
+    maximum climbs far above its first tile's, so the fixed-reference kernel marks the unit
+    and the exact kernel recomputes it; the other units stay on the fast path.  Both kinds
+    are in this call and every row matches the oracle."""
+    T, Hq = 4, 64
+    lengths = [5000, 20000]
+    mla = W.make_mla_decode(79, lengths=lengths, q_per_seq=T, num_q_heads=Hq, q_mult=2.0)
+    n_over = n_units = 0
+    for s in range(len(lengths)):
+        L = lengths[s]
+        codes = oracle.gather_paged(mla.kv_pool, mla.block_table[s], L)
+        sc = oracle.gather_paged(mla.kv_scale[..., None], mla.block_table[s], L)[:, 0]
+        k = oracle.mla_dequant(codes, sc)
+        q = oracle.bf16_to_f64(mla.q_rows(s)).reshape(T * Hq, 576)
+        pos = np.repeat(mla.q_pos(s), Hq)
+        sl = (q @ k.T) * (mla.scale / np.log(2.0))
+        sl[np.arange(L)[None, :] > pos[:, None]] = -np.inf
+        for k0 in range(0, L, 4096):
+            ov = _tile_overflow(sl[:, k0:k0 + 4096]).reshape(2, 128)    # two 128-row units
+            n_units += 2
+            n_over += int(ov.any(axis=1).sum())
+    assert 0 < n_over < n_units, (n_over, n_units)
+    dev = MlaOnDevice(mla)
+    out, lse = _mla_decode(pa_lib, dev, T)
+    got = bf16_out(out).reshape(len(lengths) * T, Hq, 512)
+    lg = lse.cpu().numpy().reshape(len(lengths) * T, Hq)
+    for s in range(len(lengths)):
+        (ro, rl), _, _ = _mla_ref(mla, s)
+        assert_close_stress(got[s * T:(s + 1) * T], ro, FP8_MAX_ABS, FP8_L1, f"mla fallback s={s}")
+        np.testing.assert_allclose(lg[s * T:(s + 1) * T], rl, atol=LSE_ABS)
+
+
+@pytest.mark.parametrize("Hq", [64, 32, 128])
+def test_sparse_mla_fixed_reference_fallback(pa_lib, Hq):
+    """Sparse MLA with peaked queries: even query rows list their selections by ascending
+    score (later tiles' maxima can pass the first tile's by more than 2^8: the exact
+    fallback recomputes those workgroups), odd rows in random order.  The result does not depend on
+    the order; every row matches the oracle, for 32, 64 and 128 heads."""
+    import torch
+    n, k = 16, 300
+    qm = 2.4 if Hq == 32 else 2.0          # fewer heads per row: a larger spread to overflow
+    mla, idx = W.make_sparse_mla(94, lengths=[2000 + n], n_new=[n], num_q_heads=Hq, q_mult=qm)
+    L = int(mla.total_len[0])
+    codes = oracle.gather_paged(mla.kv_pool, mla.block_table[0], L)
+    sc = oracle.gather_paged(mla.kv_scale[..., None], mla.block_table[0], L)[:, 0]
+    kk = oracle.mla_dequant(codes, sc)
+    rng = np.random.default_rng(94)
+    pos = mla.q_pos(0)
+    tk = np.full((n, k), -1, np.int32)
+    over = []
+    for r in range(n):
+        sel = rng.choice(int(pos[r]) + 1, size=k, replace=False)
+        s_row = (oracle.bf16_to_f64(mla.q[r]) @ kk[sel].T) * (mla.scale / np.log(2.0))     # [Hq][k]
+        if r % 2 == 0:
+            sel = sel[np.argsort(s_row.max(axis=0), kind="stable")]
+            s_row = (oracle.bf16_to_f64(mla.q[r]) @ kk[sel].T) * (mla.scale / np.log(2.0))
+        tk[r] = sel
+        over.append(bool(_tile_overflow(s_row).any()))
+    assert any(over) and not all(over), over        # both paths in one call
+    dev = MlaOnDevice(mla, idx)
+    out = pa_lib.sparse_mla_attn(dev.q, dev.pool, dev.bt, dev.q_seq, torch.from_numpy(tk).cuda(), scale=mla.scale)
+    torch.cuda.synchronize()
+    ro, _ = oracle.sparse_mla_attention(mla.q[0:n], codes, sc, tk, mla.scale)
+    assert_close_stress(bf16_out(out), ro, FP8_MAX_ABS, FP8_L1, f"sparse fallback Hq={Hq}")
