@@ -42,8 +42,8 @@ GqaDecodeDims gqa_decode_dims(int num_seqs, int q_per_seq, int num_q_heads, int 
   d.region_cap = kPlanTiles * d.members;
   d.grid = device_cus();
   d.subs = (num_kv_heads < 8 && 8 % num_kv_heads == 0) ? 8 / num_kv_heads : 1;
-  // pieces: every region's passes cut at the workgroup boundaries
-  d.pieces_cap = d.n_groups * d.n_chunks + d.grid - 1;
+  // pieces: every group's passes cut at the workgroup boundaries
+  d.pieces_cap = d.n_groups + d.grid - 1;
   return d;
 }
 
@@ -149,12 +149,13 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(GqaDecodeArgs a) {
 
 // ---------------------------------------------------------------------------------
 // 2. Scan (one workgroup): region_start[r] = passes of the regions before r in region order
-// (the compact pass numbering; region_start[R] = P, the total), and piece_start[r] = pieces
-// before region r.  The attention grid splits [0, P) evenly over N = min(grid, P)
-// workgroups: workgroup w < N takes passes [floor(w P / N), floor((w + 1) P / N)), never
-// an empty range (P / N >= 1).  A piece is a region's share of one workgroup's range, so
-// region r holds wg_of(last) - wg_of(first) + 1 pieces (0 when it has no pass), and the
-// pieces of a group are numbered consecutively in pass order.
+// (the compact pass numbering; region_start[R] = P, the total), and piece_start[g] = pieces
+// before group g.  A group's regions are consecutive, so its passes are one contiguous
+// range of the numbering.  The attention grid splits [0, P) over N = min(grid, P)
+// workgroups, never into an empty range (P / N >= 1).  A piece is a group's share of one
+// workgroup's range, so group g holds wg_of(last) - wg_of(first) + 1 pieces (0 when it has
+// no pass), numbered consecutively in pass order: a workgroup's range that crosses a
+// region boundary inside one group stays one piece.
 // Workgroup w of N takes passes [wg_bound(w), wg_bound(w + 1)).  Workgroups go to the 8
 // XCDs round robin (XCD = w mod 8), and the odd XCDs run the same passes about 4.5 % slower
 // (per-workgroup end stamps on MI355X, repeatable launch to launch); so when every
@@ -176,6 +177,28 @@ __device__ __forceinline__ int wg_of(long x, long P, long N) {
   return (int)w;
 }
 __device__ __forceinline__ long active_wgs(long grid, long P) { return grid < P ? grid : P; }
+
+// The region holding pass x: the first r in [0, n) with rs[r + 1] > x (one exists, since
+// rs[n] = P > x).  A wave tests 64 evenly spaced candidates per round (one load per lane),
+// so the search costs one or two dependent loads rather than log2(n).
+__device__ __forceinline__ int region_of(const int32_t* rs, int n, int x) {
+  const int lane = threadIdx.x & 63;
+  int r0 = 0, r1 = n - 1;                           // the answer lies in [r0, r1]
+  while (r0 < r1) {
+    const int span = r1 - r0 + 1, step = (span + 63) / 64;
+    const int r = r0 + lane * step;
+    const bool past = r <= r1 && rs[r + 1] > x;
+    const uint64_t bal = __ballot(past);
+    if (bal == 0) {                                 // the answer follows the last candidate
+      r0 += ((span - 1) / step) * step + 1;
+    } else {
+      const int L = __builtin_ctzll(bal);
+      r1 = r0 + L * step;
+      r0 = L == 0 ? r0 : r0 + (L - 1) * step + 1;
+    }
+  }
+  return r0;
+}
 
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -212,20 +235,21 @@ __global__ __launch_bounds__(1024) void decode_scan_kernel(GqaDecodeArgs a) {
   if (tid == 0) a.region_start[n] = running;
   __syncthreads();
   const long P = running, N = active_wgs(a.dims.grid, P);
+  const int NG = a.dims.n_groups, NC = a.dims.n_chunks;
   int pieces = 0;
-  for (int base = 0; base < n; base += 1024) {
-    const int r = base + tid;
+  for (int base = 0; base < NG; base += 1024) {
+    const int g = base + tid;
     int cnt = 0;
-    if (r < n) {
-      const int s0 = a.region_start[r], s1 = a.region_start[r + 1];
+    if (g < NG) {
+      const int s0 = a.region_start[g * NC], s1 = a.region_start[(g + 1) * NC];
       cnt = s1 > s0 ? wg_of(s1 - 1, P, N) - wg_of(s0, P, N) + 1 : 0;
     }
     int total;
     const int off = block_exclusive_scan(cnt, wsum, &total);
-    if (r < n) a.piece_start[r] = pieces + off;
+    if (g < NG) a.piece_start[g] = pieces + off;
     pieces += total;
   }
-  if (tid == 0) a.piece_start[n] = pieces;
+  if (tid == 0) a.piece_start[NG] = pieces;
 }
 
 // ---------------------------------------------------------------------------------
@@ -283,7 +307,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const size_t head_stride = (size_t)16 * D;
   uint16_t* vs = sm.v[wave];
   uint16_t* qs = sm.q[wave];
-  const int n_regions = a.dims.n_groups * a.dims.n_chunks;
+  const int NG = a.dims.n_groups, NC = a.dims.n_chunks, n_regions = NG * NC;
   const long P = a.region_start[n_regions];
   const long N = active_wgs(gridDim.x, P);
   const int w = blockIdx.x;
@@ -293,24 +317,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // and heads wave, wave + 8, ...
   const int sub = NS > 1 ? wave / Hkv : 0;
   const int h_first = NS > 1 ? wave % Hkv : wave;
-  // first region holding pass lo: the first r with region_start[r + 1] > lo
-  int rlo = 0, rhi = n_regions - 1;
-  while (rlo < rhi) {
-    const int mid = (rlo + rhi) >> 1;
-    if (a.region_start[mid + 1] > lo) rhi = mid; else rlo = mid + 1;
-  }
+  const int rlo = region_of(a.region_start, n_regions, lo);
   const int m16 = lane & 15, gq = (lane >> 4) & 1;
 
-  for (int r = rlo; r < n_regions; ++r) {
-    const int s_r = a.region_start[r], s_r1 = a.region_start[r + 1];
-    if (s_r >= hi) break;
-    const int x0 = max(s_r, lo), x1 = min(s_r1, hi);
-    if (x0 >= x1) continue;                         // a region with no pass
-    const int grp = r / a.dims.n_chunks;
-    const int piece = a.piece_start[r] + (w - wg_of(s_r, P, N));
-    const size_t pass_base = (size_t)r * a.dims.region_cap;
-    const int px0 = x0 - s_r + (int)((long)(x1 - x0) * sub / NS);
-    const int px1 = x0 - s_r + (int)((long)(x1 - x0) * (sub + 1) / NS);
+  // The groups meeting [lo, hi), one piece each: passes px0 .. px1 - 1 of the compact
+  // numbering (this wave's sub-range of the group's share), which may cross the group's
+  // region boundaries.
+  for (int grp = rlo / NC; grp < NG; ++grp) {
+    const int gs = a.region_start[grp * NC], ge = a.region_start[(grp + 1) * NC];
+    if (gs >= hi) break;
+    const int x0 = max(gs, lo), x1 = min(ge, hi);
+    if (x0 >= x1) continue;                         // a group with no pass
+    const int piece = a.piece_start[grp] + (w - wg_of(gs, P, N));
+    const int px0 = x0 + (int)((long)(x1 - x0) * sub / NS);
+    const int px1 = x0 + (int)((long)(x1 - x0) * (sub + 1) / NS);
+    // a region at or before the one holding px0 (rlo holds lo <= px0; a later group's
+    // first pass is in its first region)
+    const int rc0 = max(grp * NC, rlo);
+    const int rc0_s = __builtin_amdgcn_readfirstlane(a.region_start[rc0]);
+    const int rc0_e = __builtin_amdgcn_readfirstlane(a.region_start[rc0 + 1]);
     const int s = grp * M + m;
     const bool row_ok = (m < M) && (s < a.num_seqs);
     const int L = row_ok ? min(max(a.context_len[s], 0), a.max_context_len) : 0;
@@ -325,15 +350,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
       float m_run = -INFINITY, l_run = 0.f;
 
-      // ---- passes px0 .. px1 - 1 of region r; the descriptor of the next pass to issue
-      // is loaded one pass ahead
-      int it = px0;
-      u32x4 dnext = it < px1 ? ld16(a.passes + (pass_base + it) * 4) : u32x4{0, 0, 0, 0};
+      // ---- passes px0 .. px1 - 1; the descriptor of the next pass to issue is loaded one
+      // pass ahead.  Passes [rs0, rs1) of the numbering are region rc's, stored from
+      // rc * region_cap; a pass past rs1 moves the cursor on (it stays inside the group:
+      // every pass below px1 <= ge belongs to one of its regions).
+      int it = px0, rc = rc0, rs0 = rc0_s, rs1 = rc0_e;
+      auto pass_desc = [&]() -> u32x4 {
+        while (rs1 <= it) {
+          ++rc;
+          rs0 = rs1;
+          rs1 = __builtin_amdgcn_readfirstlane(a.region_start[rc + 1]);
+        }
+        return ld16(a.passes + ((size_t)rc * a.dims.region_cap + (it - rs0)) * 4);
+      };
+      u32x4 dnext = it < px1 ? pass_desc() : u32x4{0, 0, 0, 0};
       auto next_pass = [&](Pass& Pp) -> bool {
         if (it >= px1) return false;
         const u32x4 d = dnext;
         ++it;
-        if (it < px1) dnext = ld16(a.passes + (pass_base + it) * 4);
+        if (it < px1) dnext = pass_desc();
         const uint32_t d0 = __builtin_amdgcn_readfirstlane(d.x);
         Pp.kb = (int)(d0 & ~31u);
         Pp.nv = (int)(d0 & 31u) + 1;
@@ -590,7 +625,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const int Hq = a.rows / a.q_per_seq, G = Hq / a.num_kv_heads, R = a.q_per_seq * G;
     const int t = row / Hq, hq = row % Hq, head = hq / G;
     const int g = s / a.members, m = s % a.members;
-    const int u0 = a.piece_start[g * a.n_chunks], u1 = a.piece_start[(g + 1) * a.n_chunks];
+    const int u0 = a.piece_start[g], u1 = a.piece_start[g + 1];
     n = (u1 - u0) * a.subs;
     base = ((size_t)u0 * a.subs * a.num_kv_heads + head) * 32 + m * R + t * G + hq % G;
     stride = (long)a.num_kv_heads * 32;

@@ -175,7 +175,7 @@ DecodeLayout decode_layout(int num_seqs, int q_per_seq, int num_q_heads, int max
   l.pass_bytes = round_up(regions * l.dims.region_cap * 16, 256);
   l.npass_bytes = round_up(regions * sizeof(int32_t), 256);
   l.rstart_bytes = round_up((regions + 1) * sizeof(int32_t), 256);
-  l.pstart_bytes = round_up((regions + 1) * sizeof(int32_t), 256);
+  l.pstart_bytes = round_up(((size_t)l.dims.n_groups + 1) * sizeof(int32_t), 256);
   return l;
 }
 
@@ -385,7 +385,6 @@ static pa_status decode_impl(const void* q, const pa_kv_pool* pool, const int32_
     c.piece_start = a.piece_start;
     c.subs = l.dims.subs;
     c.members = l.dims.members;
-    c.n_chunks = l.dims.n_chunks;
     c.num_kv_heads = pool->num_kv_heads;
     c.q_per_seq = q_per_seq;
   } else {
@@ -742,8 +741,10 @@ pa_status pa_profile_enable(int32_t max_records) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   for (hipEvent_t e : g_prof_events) (void)hipEventDestroy(e);
   g_prof_events.assign(2 * (size_t)max_records, nullptr);
+  // Timing-only events: without the system-scope fence a record neither writes back nor
+  // invalidates the caches, so the instrumentation does not slow the launches it brackets.
   for (auto& e : g_prof_events)
-    if (hipEventCreate(&e) != hipSuccess) {
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
       g_prof_events.clear();
       return fail(PA_ERR_HIP, "hipEventCreate failed");
     }

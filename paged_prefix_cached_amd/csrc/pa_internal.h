@@ -28,7 +28,7 @@ struct GqaDecodeDims {
   int32_t region_cap;   // pass capacity of one (group, chunk) region: kPlanTiles * members
   int32_t grid;         // attention workgroups: one per compute unit
   int32_t subs;         // sub-ranges per (piece, KV head): 8 / Hkv when Hkv divides 8, else 1
-  int32_t pieces_cap;   // upper bound of pieces: regions + grid - 1
+  int32_t pieces_cap;   // upper bound of pieces: groups + grid - 1
 };
 GqaDecodeDims gqa_decode_dims(int num_seqs, int q_per_seq, int num_q_heads, int num_kv_heads,
                               int max_context_len);
@@ -73,7 +73,7 @@ struct GqaDecodeArgs {
   int32_t* n_passes;    // [n_groups * n_chunks]
   int32_t* region_start;  // [n_groups * n_chunks + 1]: compact index of each region's first
                           //   pass; the total last
-  int32_t* piece_start;   // [n_groups * n_chunks + 1]: first piece of each region; total last
+  int32_t* piece_start;   // [n_groups + 1]: first piece of each group; total last
   int32_t bt_stride, num_seqs, q_per_seq, num_q_heads, num_kv_heads, head_dim, num_blocks;
   int32_t max_context_len;
   GqaDecodeDims dims;
@@ -91,7 +91,7 @@ struct CombineArgs {
   // of its group (subs partials each); otherwise partials are [S][max_splits][rows] with
   // split `split`.
   const int32_t* piece_start;
-  int32_t members, n_chunks, num_kv_heads, q_per_seq, subs;
+  int32_t members, num_kv_heads, q_per_seq, subs;
   // Split-K prefill partials (pf_q_start != null): workgroup (s, j, head) merges the
   // partials of new token j of sequence s, written at [s * pf_max_new + j][split][rows]
   // (rows = heads), and writes output row q_start[s] + j.

@@ -91,12 +91,12 @@ def _decode(lib, pool, ws=None, wsb=0, **kw):
 def test_decode_validation(lib):
     pool = _gqa_pool(head_dim_qk=128, head_dim_v=128)
     need = lib.paged_attn_decode_workspace_size(64, 1, 32, 142000, ctypes.byref(pool))
-    # pass-balanced decode: partials for every (region, workgroup) piece -- 8 groups of 8
-    # sequences x ceil(142000 / 8192) regions, plus one per workgroup boundary (a
-    # workgroup per compute unit; 256 when no device is visible) -- per KV head, 32 rows of
-    # (128 + 1) floats, plus the pass lists (16 B per (member, 32-key tile) slot).
+    # pass-balanced decode: partials for every (group, workgroup) piece -- 8 groups of 8
+    # sequences, plus one per workgroup boundary (a workgroup per compute unit; 256 when no
+    # device is visible) -- per KV head, 32 rows of (128 + 1) floats, plus the pass lists
+    # (16 B per (member, 32-key tile) slot of each of the 8 x ceil(142000 / 8192) regions).
     regions = 8 * -(-142000 // 8192)
-    partials = (regions + 256 - 1) * 8 * 32 * 129 * 4
+    partials = (8 + 256 - 1) * 8 * 32 * 129 * 4
     passes = regions * 256 * 8 * 16
     assert partials + passes <= need <= partials + passes + 64 * 1024
     assert need <= lib.paged_attn_decode_noalloc_max_bytes()        # the benchmark batch fits

@@ -61,7 +61,7 @@ def test_noalloc_rejects_sizes_beyond_its_scratch(pa_lib):
     wl = W.make_gqa_decode(205, n_sessions=1, members=2, lo=100, hi=200)
     dev = GqaOnDevice(wl)
     S = wl.num_seqs
-    big_ctx = 2_000_000                      # a bound whose workspace exceeds the scratch
+    big_ctx = 16_000_000                     # a bound whose workspace (pass lists) exceeds the scratch
     bt = torch.full((S, big_ctx // 16), -1, dtype=torch.int32, device="cuda")
     need = pa_lib.load().paged_attn_decode_workspace_size(S, 1, 32, big_ctx, pa_lib.ctypes.byref(dev.pool))
     assert need > pa_lib.load().paged_attn_decode_noalloc_max_bytes()
