@@ -352,6 +352,13 @@ pa_status pa_test_topk_from_scores(const float* scores, const int32_t* valid_len
  * pa_profile_enable(max_records): from now on, every kernel the library launches (up to
  *   max_records launches) is bracketed by two hipEvents recorded on the call's stream.
  *   Creates 2*max_records events (no device memory is allocated); resets the records.
+ *   The events are timing-only (created with hipEventDisableSystemFence): a record
+ *   writes back and invalidates no cache, yet each still costs the stream a few
+ *   microseconds, so a step that must be timed as a whole brackets only the launch it
+ *   reports.
+ * pa_profile_select(name): records only launches of that kernel name (see below); NULL
+ *   or "" records every launch again.  PA_ERR_INVALID_ARG for a name of 64 characters or
+ *   more.  pa_profile_disable clears the selection.
  * pa_profile_count(): number of launches recorded so far.
  * pa_profile_record(i, name, cap, ms): waits for record i and returns its kernel name
  *   ("prefill_gqa", "decode_gqa", "decode_mla", "combine", "indexer", "topk",
@@ -359,6 +366,7 @@ pa_status pa_test_topk_from_scores(const float* scores, const int32_t* valid_len
  * pa_profile_disable(): stops recording and destroys the events.
  * ------------------------------------------------------------------------------- */
 pa_status pa_profile_enable(int32_t max_records);
+pa_status pa_profile_select(const char* name);
 int32_t pa_profile_count(void);
 pa_status pa_profile_record(int32_t i, char* name_out, int32_t name_cap, float* ms_out);
 pa_status pa_profile_disable(void);

@@ -23,7 +23,7 @@ __all__ = ["load", "PAError", "KVPool", "gqa_pool", "mla_pool", "indexer_pool", 
            "paged_attn_prefill", "paged_attn_decode", "paged_attn_decode_noalloc", "mla_indexer_topk",
            "sparse_mla_attn",
            "paged_kv_append", "pa_test_gather_kv", "pa_test_topk_from_scores", "pa_profile_enable",
-           "pa_profile_records", "pa_profile_disable", "LIB_PATH"]
+           "pa_profile_select", "pa_profile_records", "pa_profile_disable", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 PA_BF16, PA_FP8_E4M3, PA_PACKED_MLA = 1, 2, 3
@@ -67,6 +67,7 @@ _SIGS = {
     "pa_test_topk_workspace_size": (_c_sz, [_c_i32, _c_i32]),
     "pa_test_topk_from_scores": (_c_i32, [_vp, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, _vp]),
     "pa_profile_enable": (_c_i32, [_c_i32]),
+    "pa_profile_select": (_c_i32, [ctypes.c_char_p]),
     "pa_profile_count": (_c_i32, []),
     "pa_profile_record": (_c_i32, [_c_i32, ctypes.c_char_p, _c_i32, ctypes.POINTER(_c_f)]),
     "pa_profile_disable": (_c_i32, []),
@@ -257,6 +258,11 @@ def paged_kv_append(pool: KVPool, block_table, cached_len, new_len, q_start, k_n
 
 def pa_profile_enable(max_records: int) -> None:
     _check(load().pa_profile_enable(max_records), "pa_profile_enable")
+
+
+def pa_profile_select(name: str | None) -> None:
+    """Record only launches of kernel `name` (None: every launch)."""
+    _check(load().pa_profile_select(name.encode() if name else None), "pa_profile_select")
 
 
 def pa_profile_records():

@@ -44,6 +44,7 @@ GqaDecodeDims gqa_decode_dims(int num_seqs, int q_per_seq, int num_q_heads, int 
   d.subs = (num_kv_heads < 8 && 8 % num_kv_heads == 0) ? 8 / num_kv_heads : 1;
   // pieces: every group's passes cut at the workgroup boundaries
   d.pieces_cap = d.n_groups + d.grid - 1;
+  d.scan_in_kernel = (long)d.n_groups * d.n_chunks + d.n_groups + 2 <= kDecodeIdxLds;
   return d;
 }
 
@@ -72,30 +73,34 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(GqaDecodeArgs a) {
   if (tid < 32) {
     int L = 0;
     if (tid < M && s0 + tid < a.num_seqs) L = min(max(a.context_len[s0 + tid], 0), a.max_context_len);
-    len_s[tid] = L;
+    len_s[tid] = L;                     // read after the scan's barrier below
   }
-  __syncthreads();
   const int tile = c * kPlanTiles + tid, kb = tile * kTile;
+  const int ia = min(2 * tile, a.bt_stride - 1), ib = min(2 * tile + 1, a.bt_stride - 1);
   uint32_t part = 0;                    // members taking part in this tile
   for (int m0 = 0; m0 < M; m0 += 8) {   // 8 members' loads in flight at a time
-    int ra[8], rb[8], nl[8];
+    int ra[8], rb[8], Lm[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {       // unconditional loads (entry 0 when unused)
+    for (int i = 0; i < 8; ++i) {
+      // The lengths and the table entries load together: the entries come from an existing
+      // row at clamped columns, so they stay in bounds whatever the lengths turn out to be,
+      // and only those inside the member's blocks are used.
       const int mm = m0 + i;
-      const int L = mm < M ? len_s[mm] : 0;
-      const bool ok = kb < L;
-      nl[i] = ok ? (L + 15) >> 4 : 0;
-      const int32_t* row = a.bt + (ok ? (size_t)(s0 + mm) * a.bt_stride : 0);
-      ra[i] = row[ok ? 2 * tile : 0];
-      rb[i] = row[2 * tile + 1 < nl[i] ? 2 * tile + 1 : 0];
-      if (ok) part |= 1u << mm;
+      const bool real = mm < M && s0 + mm < a.num_seqs;
+      Lm[i] = real ? min(max(a.context_len[s0 + mm], 0), a.max_context_len) : 0;
+      const int32_t* row = a.bt + (size_t)min(s0 + mm, a.num_seqs - 1) * a.bt_stride;
+      ra[i] = row[ia];
+      rb[i] = row[ib];
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (m0 + i >= M) break;
+      const bool ok = kb < Lm[i];
+      const int nl = ok ? (Lm[i] + 15) >> 4 : 0;
+      if (ok) part |= 1u << (m0 + i);
       int2 p = {-1, -1};
-      if (2 * tile < nl[i] && ra[i] >= 0 && ra[i] < a.num_blocks) p.x = ra[i];
-      if (2 * tile + 1 < nl[i] && rb[i] >= 0 && rb[i] < a.num_blocks) p.y = rb[i];
+      if (2 * tile < nl && ra[i] >= 0 && ra[i] < a.num_blocks) p.x = ra[i];
+      if (2 * tile + 1 < nl && rb[i] >= 0 && rb[i] < a.num_blocks) p.y = rb[i];
       pr[m0 + i][tid] = p;
     }
   }
@@ -200,6 +205,8 @@ __device__ __forceinline__ int region_of(const int32_t* rs, int n, int x) {
   return r0;
 }
 
+// Exclusive prefix sum over a workgroup of NW waves; *total = the sum over all threads.
+template <int NW>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int x = v;
@@ -211,7 +218,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
   int off = x - v, t = 0;
-  for (int w = 0; w < 16; ++w) {
+  for (int w = 0; w < NW; ++w) {
     off += w < wave ? wsum[w] : 0;
     t += wsum[w];
   }
@@ -228,7 +235,7 @@ __global__ __launch_bounds__(1024) void decode_scan_kernel(GqaDecodeArgs a) {
   for (int base = 0; base < n; base += 1024) {
     const int r = base + tid;
     int total;
-    const int off = block_exclusive_scan(r < n ? a.n_passes[r] : 0, wsum, &total);
+    const int off = block_exclusive_scan<16>(r < n ? a.n_passes[r] : 0, wsum, &total);
     if (r < n) a.region_start[r] = running + off;
     running += total;
   }
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(1024) void decode_scan_kernel(GqaDecodeArgs a) {
       cnt = s1 > s0 ? wg_of(s1 - 1, P, N) - wg_of(s0, P, N) + 1 : 0;
     }
     int total;
-    const int off = block_exclusive_scan(cnt, wsum, &total);
+    const int off = block_exclusive_scan<16>(cnt, wsum, &total);
     if (g < NG) a.piece_start[g] = pieces + off;
     pieces += total;
   }
@@ -284,7 +291,7 @@ struct Pass {
   bool in;
 };
 
-template <int D>
+template <int D, bool IDX_LDS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gqa_decode_kernel(GqaDecodeArgs a) {
   constexpr int KS = D / 16;   // QK k-steps (32x32x16)
   constexpr int MT = D / 32;   // O^T tiles of 32 dims
@@ -293,6 +300,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   using Sm = DecodeSmem<D>;
   __shared__ __attribute__((aligned(16))) Sm sm;
   __shared__ int prog[kWaves];
+  __shared__ int idx_s[kDecodeIdxLds];
+  __shared__ int wsum_s[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -308,7 +317,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   uint16_t* vs = sm.v[wave];
   uint16_t* qs = sm.q[wave];
   const int NG = a.dims.n_groups, NC = a.dims.n_chunks, n_regions = NG * NC;
-  const long P = a.region_start[n_regions];
+  // Region starts (n_regions + 1) and group piece starts (NG + 1): with IDX_LDS numbered
+  // here, in LDS, by every workgroup alike from the plan's pass counts (workgroup 0 also
+  // stores the piece starts for the combine); otherwise read from the workspace, where
+  // decode_scan_kernel numbered them (too many regions for the LDS index).  The numbering
+  // is the same either way.
+  int* const rs_l = idx_s;
+  int* const ps_l = idx_s + n_regions + 1;
+  const int32_t* const rs = IDX_LDS ? rs_l : a.region_start;
+  const int32_t* const ps = IDX_LDS ? ps_l : a.piece_start;
+  if (IDX_LDS) {
+    int running = 0;
+    for (int base = 0; base < n_regions; base += kThreads) {
+      const int r = base + tid;
+      int total;
+      const int off = block_exclusive_scan<kWaves>(r < n_regions ? a.n_passes[r] : 0, wsum_s, &total);
+      if (r < n_regions) rs_l[r] = running + off;
+      running += total;
+    }
+    if (tid == 0) rs_l[n_regions] = running;
+    __syncthreads();                                // rs_l complete
+    const long P0 = running, N0 = active_wgs(gridDim.x, P0);
+    int pieces = 0;
+    for (int base = 0; base < NG; base += kThreads) {
+      const int g = base + tid;
+      int cnt = 0;
+      if (g < NG) {
+        const int s0 = rs_l[g * NC], s1 = rs_l[(g + 1) * NC];
+        cnt = s1 > s0 ? wg_of(s1 - 1, P0, N0) - wg_of(s0, P0, N0) + 1 : 0;
+      }
+      int total;
+      const int off = block_exclusive_scan<kWaves>(cnt, wsum_s, &total);
+      if (g < NG) ps_l[g] = pieces + off;
+      pieces += total;
+    }
+    if (tid == 0) ps_l[NG] = pieces;
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int g = tid; g <= NG; g += kThreads) a.piece_start[g] = ps_l[g];
+  }
+  const long P = rs[n_regions];
   const long N = active_wgs(gridDim.x, P);
   const int w = blockIdx.x;
   if (w >= N) return;                               // fewer passes than workgroups
@@ -317,25 +365,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // and heads wave, wave + 8, ...
   const int sub = NS > 1 ? wave / Hkv : 0;
   const int h_first = NS > 1 ? wave % Hkv : wave;
-  const int rlo = region_of(a.region_start, n_regions, lo);
+  const int rlo = region_of(rs, n_regions, lo);
   const int m16 = lane & 15, gq = (lane >> 4) & 1;
 
   // The groups meeting [lo, hi), one piece each: passes px0 .. px1 - 1 of the compact
   // numbering (this wave's sub-range of the group's share), which may cross the group's
   // region boundaries.
   for (int grp = rlo / NC; grp < NG; ++grp) {
-    const int gs = a.region_start[grp * NC], ge = a.region_start[(grp + 1) * NC];
+    const int gs = rs[grp * NC], ge = rs[(grp + 1) * NC];
     if (gs >= hi) break;
     const int x0 = max(gs, lo), x1 = min(ge, hi);
     if (x0 >= x1) continue;                         // a group with no pass
-    const int piece = a.piece_start[grp] + (w - wg_of(gs, P, N));
+    const int piece = ps[grp] + (w - wg_of(gs, P, N));
     const int px0 = x0 + (int)((long)(x1 - x0) * sub / NS);
     const int px1 = x0 + (int)((long)(x1 - x0) * (sub + 1) / NS);
     // a region at or before the one holding px0 (rlo holds lo <= px0; a later group's
     // first pass is in its first region)
     const int rc0 = max(grp * NC, rlo);
-    const int rc0_s = __builtin_amdgcn_readfirstlane(a.region_start[rc0]);
-    const int rc0_e = __builtin_amdgcn_readfirstlane(a.region_start[rc0 + 1]);
+    const int rc0_s = __builtin_amdgcn_readfirstlane(rs[rc0]);
+    const int rc0_e = __builtin_amdgcn_readfirstlane(rs[rc0 + 1]);
     const int s = grp * M + m;
     const bool row_ok = (m < M) && (s < a.num_seqs);
     const int L = row_ok ? min(max(a.context_len[s], 0), a.max_context_len) : 0;
@@ -359,7 +407,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         while (rs1 <= it) {
           ++rc;
           rs0 = rs1;
-          rs1 = __builtin_amdgcn_readfirstlane(a.region_start[rc + 1]);
+          rs1 = __builtin_amdgcn_readfirstlane(rs[rc + 1]);
         }
         return ld16(a.passes + ((size_t)rc * a.dims.region_cap + (it - rs0)) * 4);
       };
@@ -575,16 +623,20 @@ hipError_t launch_gqa_decode_plan(const GqaDecodeArgs& a, hipStream_t stream) {
   const unsigned regions = (unsigned)a.dims.n_groups * a.dims.n_chunks;
   if (regions == 0) return hipSuccess;
   hipLaunchKernelGGL(decode_plan_kernel, dim3(regions), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(decode_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
+  if (!a.dims.scan_in_kernel) hipLaunchKernelGGL(decode_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gqa_decode(const GqaDecodeArgs& a, hipStream_t stream) {
   if (a.dims.n_groups == 0 || a.dims.n_chunks == 0) return hipSuccess;
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL((gqa_decode_kernel<128>), dim3(a.dims.grid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((gqa_decode_kernel<64>), dim3(a.dims.grid), dim3(kThreads), 0, stream, a);
+  const dim3 grid(a.dims.grid), block(kThreads);
+  if (a.head_dim == 128) {
+    if (a.dims.scan_in_kernel) hipLaunchKernelGGL((gqa_decode_kernel<128, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gqa_decode_kernel<128, false>), grid, block, 0, stream, a);
+  } else {
+    if (a.dims.scan_in_kernel) hipLaunchKernelGGL((gqa_decode_kernel<64, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gqa_decode_kernel<64, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

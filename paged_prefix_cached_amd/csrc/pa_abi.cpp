@@ -118,6 +118,7 @@ struct ProfRec {
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+char g_prof_only[64] = "";                // empty: every launch is recorded
 std::vector<hipEvent_t> g_prof_events;   // 2 per record slot
 std::vector<ProfRec> g_prof_recs;
 
@@ -126,7 +127,8 @@ hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
   int slot = -1;
   {
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    if (g_prof_on && g_prof_recs.size() * 2 < g_prof_events.size()) {
+    if (g_prof_on && g_prof_recs.size() * 2 < g_prof_events.size() &&
+        (g_prof_only[0] == 0 || strcmp(g_prof_only, name) == 0)) {
       slot = (int)g_prof_recs.size();
       g_prof_recs.push_back({name, slot});
     }
@@ -753,6 +755,15 @@ pa_status pa_profile_enable(int32_t max_records) {
   return PA_OK;
 }
 
+pa_status pa_profile_select(const char* name) {
+  g_detail[0] = 0;
+  if (name != nullptr && strlen(name) >= sizeof(g_prof_only))
+    return fail(PA_ERR_INVALID_ARG, "kernel name longer than %zu characters", sizeof(g_prof_only) - 1);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  snprintf(g_prof_only, sizeof(g_prof_only), "%s", name != nullptr ? name : "");
+  return PA_OK;
+}
+
 int32_t pa_profile_count(void) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   return (int32_t)g_prof_recs.size();
@@ -774,6 +785,7 @@ pa_status pa_profile_record(int32_t i, char* name_out, int32_t name_cap, float* 
 pa_status pa_profile_disable(void) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = false;
+  g_prof_only[0] = 0;
   for (hipEvent_t e : g_prof_events) (void)hipEventDestroy(e);
   g_prof_events.clear();
   g_prof_recs.clear();

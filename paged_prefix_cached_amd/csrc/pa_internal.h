@@ -15,6 +15,8 @@ constexpr int kDecodeSplitMla = PA_DECODE_SPLIT_MLA;
 
 // GQA decode: the plan covers kPlanTiles 32-key tiles of a group per workgroup (a region).
 constexpr int kPlanTiles = 256;
+// Ints of LDS the GQA decode kernel sets aside for region and piece starts.
+constexpr int kDecodeIdxLds = 4096;
 
 // Compute units of the current device (read once per device): the GQA decode grid and the
 // prefill split decision depend on it, so workspace queries and calls agree.
@@ -29,6 +31,9 @@ struct GqaDecodeDims {
   int32_t grid;         // attention workgroups: one per compute unit
   int32_t subs;         // sub-ranges per (piece, KV head): 8 / Hkv when Hkv divides 8, else 1
   int32_t pieces_cap;   // upper bound of pieces: groups + grid - 1
+  int32_t scan_in_kernel;  // 1: every attention workgroup numbers the passes and pieces
+                           //   itself, in LDS (regions + groups + 2 <= kDecodeIdxLds);
+                           //   0: decode_scan_kernel numbers them in the workspace
 };
 GqaDecodeDims gqa_decode_dims(int num_seqs, int q_per_seq, int num_q_heads, int num_kv_heads,
                               int max_context_len);

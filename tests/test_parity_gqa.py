@@ -125,6 +125,36 @@ def test_decode_edge_lengths_and_determinism(pa_lib):
         assert_close(got[s:s + 1], ro, BF16_MAX_ABS, BF16_L1, f"decode L={lengths[s]}")
 
 
+def test_decode_plan_beyond_the_lds_index(pa_lib):
+    """A context bound of 1,000,000 tokens over 34 groups of 2 sequences (2 query tokens x 8
+    heads per KV head: 16 rows each) makes 34 x 123 plan regions: more region and piece
+    starts than the attention kernel's 4,096-int LDS index holds, so the separate
+    scan kernel numbers them in the workspace.  The actual contexts are short, so the
+    regions past them are empty: the partition, and hence the output, is bit-identical to
+    the same call under the tight bound (numbered in LDS), and both match the oracle."""
+    import torch
+    T, Hq, Hkv, S = 2, 16, 2, 68
+    lengths = [int(x) for x in np.random.default_rng(71).integers(40, 3000, S)]
+    wl = W.make_gqa(71, lengths=lengths, n_new=[T] * S, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128)
+    dev = GqaOnDevice(wl)
+    big = 1_000_000
+    groups = S // 2
+    assert groups * -(-big // 8192) + groups + 2 > 4096 and groups * -(-dev.max_total // 8192) + groups + 2 <= 4096
+    bt_wide = torch.full((S, big // 16), -1, dtype=torch.int32, device="cuda")
+    bt_wide[:, :dev.bt.shape[1]] = dev.bt
+    q = dev.q.view(S, T, Hq, 128)
+    outs = []
+    for bt, bound in ((dev.bt, dev.max_total), (bt_wide, big)):
+        outs.append(pa_lib.paged_attn_decode(q, dev.pool, bt, dev.total_len, q_per_seq=T, num_q_heads=Hq,
+                                             max_context_len=bound, scale=wl.scale))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    got = bf16_out(outs[1]).reshape(S * T, Hq, 128)
+    for s in range(S):
+        ro, _ = oracle.paged_gqa_attention(wl, s)
+        assert_close(got[s * T:(s + 1) * T], ro, BF16_MAX_ABS, BF16_L1, f"decode wide plan seq={s}")
+
+
 def test_decode_full_size_sampled(pa_lib):
     """The benchmarked decode workload at full size (64 sequences, 8 sessions, contexts
     4K-142K); a sample of sequences is checked against the oracle."""
