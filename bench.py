@@ -92,7 +92,8 @@ def timed_steps(step, steps, warmup, only=None):
         step()
     torch.cuda.synchronize()
     pa.pa_profile_enable(64 * max(1, steps))
-    pa.pa_profile_select(only)
+    if only:
+        pa.pa_profile_select(only)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()

@@ -275,9 +275,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   const int my_loads = kLoadsMax + (wave == NW - 1 ? 1 : 0);
 
   f32x16 acc[kMT];
-  // m_run: the row's reference maximum (log2 units), set at its first valid key and fixed
-  float m_run = -INFINITY, l_run = 0.f;
-  bool ovf = false;                                   // some row's maximum passed m_run + kSlack
+  // m_run: the row's reference maximum (log2 units), set at its first valid key and fixed;
+  // u_max: the largest scaled dot product s * scale_t this lane has seen (its half of the
+  // row's keys), checked against m_run + kSlack once, after the last tile
+  float m_run = -INFINITY, l_run = 0.f, u_max = -INFINITY;
+  bool all_set = false;                               // every row of the wave has its m_run
   // max / sum of a value over lanes l and l ^ 32 (the two halves of a row's keys)
   auto halves = [](float v) {
     return __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -341,43 +343,59 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   };
   // scale, mask and softmax of tile t (buffer B); lane holds row `row`, keys 8 (i / 4) +
   // 4 h + i % 4; P as fp16 B operands, k-step kk holding keys 16 kk + 8 (j / 4) + 4 h + j % 4
+  //
+  // Once every row of the wave has its reference (all_set, usually from the first tile on)
+  // the softmax is elementwise: no reduction across lanes, no guard for a row without one,
+  // and no clamp -- a row whose p would pass 2^kSlack is caught by the v_max check at the
+  // end, and its work unit is recomputed exactly, so what it accumulated is never used.
+  // Tiles whose keys are all visible (the common case) skip the mask.
+  // In log2 units a score is v = u * scale_log2 with u = s * scale_t, and p = 2^(v - m_run)
+  // is evaluated as exp2(fma(u, scale_log2, -m_run)).
   auto softmax = [&](int B, int t, const f32x16& s0, u32x4 (&pb)[2]) {
     uint32_t okm = tmask[B];
     if constexpr (!SPARSE) {
       const int lim = pos - (k_begin + t * kKT) + 1;  // causal: keys k < lim are visible
       okm &= lim >= 32 ? ~0u : (lim <= 0 ? 0u : ((1u << lim) - 1u));
     }
+    const bool full = __ballot(okm != ~0u) == 0;     // every row sees all 32 keys
     okm >>= 4 * h;
-    float sv[16];
+    // this lane's keys 8 q4 + 4 h + i: scales, then u (masked keys -inf)
+    f32x4 sc[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) sc[q4] = *reinterpret_cast<const f32x4*>(&tsc[B][8 * q4 + 4 * h]);
+    float u[16];
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) u[i] = s0[i] * sc[i / 4][i % 4];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        u[i] = ((okm >> (8 * (i / 4) + i % 4)) & 1u) ? s0[i] * sc[i / 4][i % 4] : -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 sc = *reinterpret_cast<const f32x4*>(&tsc[B][8 * q4 + 4 * h]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = (okm >> (8 * q4 + i)) & 1u;
-        const float v = ok ? s0[4 * q4 + i] * (sc[i] * scale_log2) : -INFINITY;
-        sv[4 * q4 + i] = v;
-        mx = fmaxf(mx, v);
-      }
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, u[i]);
+    u_max = fmaxf(u_max, mx);
+    float m_sub = m_run;
+    if (!all_set) {
+      // some row still lacks a reference: take it from this tile's row maximum (a row with
+      // no visible key so far keeps -inf, and its p are 0)
+      const float row_mx = halves_max(mx);
+      if (m_run == -INFINITY) m_run = row_mx * scale_log2;
+      m_sub = m_run == -INFINITY ? 0.f : m_run;
+      all_set = __ballot(m_run == -INFINITY) == 0;
     }
-    mx = halves_max(mx);
-    m_run = m_run == -INFINITY ? mx : m_run;          // nothing accumulated before the first
-    ovf |= mx > m_run + kSlack;
     float rs = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       float pvv[8];
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const f32x4 sc = *reinterpret_cast<const f32x4*>(&tsc[B][16 * kk + 8 * q2 + 4 * h]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // masked keys: p = 0; invalid keys also have a zero scale and zero V elements
-          const float p = m_run == -INFINITY ? 0.f : fast_exp2(fminf(sv[8 * kk + 4 * q2 + i] - m_run, kSlack));
-          rs += p;
-          pvv[4 * q2 + i] = p * sc[i];
-        }
+      for (int j = 0; j < 8; ++j) {
+        // masked keys: p = exp2(-inf) = 0; invalid keys also have a zero scale and zero V
+        const int i = 8 * kk + j;
+        const float p = fast_exp2(__builtin_fmaf(u[i], scale_log2, -m_sub));
+        rs += p;
+        pvv[j] = p * sc[i / 4][i % 4];
       }
       pb[kk] = u32x4{pack_f16x2(pvv[0], pvv[1]), pack_f16x2(pvv[2], pvv[3]), pack_f16x2(pvv[4], pvv[5]),
                      pack_f16x2(pvv[6], pvv[7])};
@@ -412,6 +430,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   }
   wait_vm<0>();                                       // no DMA outlives the workgroup
   {
+    const float row_umax = halves_max(u_max);
+    const bool ovf = m_run != -INFINITY && __builtin_fmaf(row_umax, scale_log2, -m_run) > kSlack;
     const bool w_ovf = __ballot(ovf) != 0;
     if (lane == 0) ovf_s[wave] = w_ovf ? 1 : 0;
   }
