@@ -22,9 +22,11 @@
 // key for every chunk pair it loads (one row address per lane and tile), the Q.K fragment
 // reads of a k-step cover 512 contiguous bytes, and the transposed V reads of a half-wave
 // hit 64 distinct banks.  Per tile a wave computes
-//   S^T = K Q^T with v_mfma_f32_32x32x16_f16: the K fragment of k-step ks (key = lane % 32,
-//     8 dims) is one ds_read_b64 of FP8 bytes, converted exactly to fp16 in registers (the
-//     gfx950 scaled converter, scale 1);
+//   S^T = K Q^T with v_mfma_f32_32x32x16_f16: lane (key r = lane % 32, half h = lane / 32)
+//     reads all 16 bytes of chunk 2 j + h of its key with one ds_read_b128 and feeds the
+//     two halves to k-steps 2 j and 2 j + 1, converted exactly to fp16 in registers (the
+//     gfx950 scaled converter, scale 1); so k-step 2 j + e covers dims 32 j + 16 h + 8 e ..
+//     + 7 of each half-wave, and the Q fragments are loaded in that order;
 //   the softmax per row (lane = row, 16 keys; one lane-half swap per reduction), the
 //     per-token scale folded into the scores (s * scale_t) and into P (p * scale_t);
 //   O^T += V^T P^T: the V^T fragment (dim = lane % 32, 8 keys) is one ds_read_b64_tr_b8 --
@@ -74,6 +76,10 @@ typedef __attribute__((address_space(3))) const uint8_t lds_u8;
 
 __device__ __forceinline__ u32x2 lds_read_b64(lds_u8* base, int off) {
   return *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(base + off);
+}
+
+__device__ __forceinline__ u32x4 lds_read_b128(lds_u8* base, int off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(base + off);
 }
 
 __device__ __forceinline__ u32x2 lds_read_tr8(lds_u8* base, int off) {
@@ -182,17 +188,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   const int n_tiles = (n_keys + kKT - 1) / kKT;
 
   // ---- this lane's query row (C column = lane % 32) and its Q fragments (fp16, B operand:
-  // k-step ks holds dims 16 ks + 8 h .. + 7)
+  // k-step 2 j + e holds dims 32 j + 16 h + 8 e .. + 7, matching the K fragments)
   const int row = row0 + wave * 32 + l32;
   const bool row_ok = row < rows_total;
   const int row_c = row_ok ? row : rows_total - 1;
   const int pos = SPARSE ? 0x7fffffff : (L - T + row_c / Hq);
   u32x4 qf[kQS];
   {
-    const uint16_t* qp = qbase + (size_t)row_c * kDqk + 8 * h;
+    const uint16_t* qp = qbase + (size_t)row_c * kDqk + 16 * h;
 #pragma unroll
     for (int ks = 0; ks < kQS; ++ks) {
-      const u32x4 v = ld16(qp + 16 * ks);
+      const u32x4 v = ld16(qp + 32 * (ks / 2) + 8 * (ks % 2));
       qf[ks] = u32x4{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
     }
   }
@@ -294,8 +300,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   };
 
   // per-lane LDS offsets (bytes, relative to a tile)
-  // K fragment of k-step ks: key l32, bytes 16 ks + 8 h = chunk ks, half h
-  const int k_even = 16 * l32 + 8 * h, k_odd = 16 * (l32 ^ 4) + 8 * h;
+  // K fragments of k-steps 2 j and 2 j + 1: chunk 2 j + h of key l32, at this row offset
+  // inside the chunk column (odd columns swap keys r and r ^ 4)
+  const int k_row = 16 * (l32 ^ (4 * h));
   // V^T fragment of output tile mt, key step kk: within each 16-lane group g = lane / 16,
   // source lane s = 2 k + hh reads key 16 kk + 4 (g / 2) + k + 4 (k / 4) at bytes
   // 32 mt + 16 (g % 2) + 8 hh (chunk 2 mt + g % 2); the lane then holds dim 32 mt + lane % 32
@@ -305,21 +312,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   const int v_base = (vg & 1) * kColB + 16 * (v_key0 ^ (4 * (vg & 1))) + 8 * vhh;   // + 256 kk + 1024 mt
   lds_u8* const lds = (lds_u8*)&raw[0][0];
 
-  // S^T = K Q^T over the 36 k-steps of tile buffer B (fragment reads kPre ahead), with the
+  // S^T = K Q^T over the 36 k-steps of tile buffer B (fragment reads kPre k-steps ahead), with the
   // row loads of the next tile spread over the pass
   auto qk = [&](int B, const Dma& d) -> f32x16 {
     const int tk = B * kTileB;
     f32x16 s0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s0[i] = 0.f;
-    u32x2 kr[kPre];
+    constexpr int kPre2 = kPre / 2;
+    u32x4 kr[kPre2];
 #pragma unroll
-    for (int j = 0; j < kPre; ++j) kr[j] = lds_read_b64(lds, tk + j * kColB + ((j & 1) ? k_odd : k_even));
+    for (int j = 0; j < kPre2; ++j) kr[j] = lds_read_b128(lds, tk + (2 * j + h) * kColB + k_row);
 #pragma unroll
     for (int i = 0; i < kQS; ++i) {
-      const u32x2 kc = kr[i % kPre];
-      const int n = i + kPre;
-      if (n < kQS) kr[i % kPre] = lds_read_b64(lds, tk + n * kColB + ((n & 1) ? k_odd : k_even));
+      const u32x4 kq = kr[(i / 2) % kPre2];
+      const u32x2 kc = (i % 2) ? u32x2{kq.z, kq.w} : u32x2{kq.x, kq.y};
+      const int n = i / 2 + kPre2;
+      if ((i % 2) && n < kQS / 2) kr[(i / 2) % kPre2] = lds_read_b128(lds, tk + (2 * n + h) * kColB + k_row);
       s0 = mfma32x32x16_f16(fp8x8_to_f16x8(kc), qf[i], s0);
       constexpr int kEvery = kQS / kLoadsMax;
       if (i % kEvery == kEvery / 2 && i / kEvery < kLoadsMax) load(d, i / kEvery);
