@@ -9,13 +9,15 @@
 //
 // A group holds M = 32 / (T*G) consecutive sequences, so its T query tokens x G heads per
 // sequence fill the 32 rows of a v_mfma_f32_32x32x16 tile (8 sequences x 4 heads for
-// 32q/8kv heads and one token).  Four launches:
+// 32q/8kv heads and one token).  Three launches (four past the LDS index):
 //   1. decode_plan_kernel lists, for every group and 32-key tile (two 16-token blocks),
 //      the DISTINCT block pairs its members reference, each with the set of members that
 //      share it and the number of its keys that hold data.  Blocks that forked sequences
 //      share become one pass for all of them: fetched from HBM once, not once per member.
-//   2. decode_scan_kernel numbers the passes of all groups consecutively (region by
-//      region) and the pieces that the attention grid cuts them into.
+//   2. The passes of all groups are numbered consecutively (region by region) and cut into
+//      pieces at the attention grid's workgroup boundaries: by every attention workgroup
+//      itself, in LDS, or -- when the region and piece starts exceed its LDS index -- by a
+//      separate decode_scan_kernel into the workspace.
 //   3. gqa_decode_kernel: one workgroup per compute unit, each taking an equal share of
 //      the pass list -- every pass costs the same (two blocks of K and V per KV head), so
 //      the shares finish together -- with one wave per KV head, so the eight waves read
