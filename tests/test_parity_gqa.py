@@ -155,6 +155,23 @@ def test_decode_plan_beyond_the_lds_index(pa_lib):
         assert_close(got[s * T:(s + 1) * T], ro, BF16_MAX_ABS, BF16_L1, f"decode wide plan seq={s}")
 
 
+def test_decode_many_groups_in_lds_numbering(pa_lib):
+    """1,100 sequences in 550 groups of two (2 query tokens x 8 heads per KV head: 16 rows
+    each): the attention workgroups' in-LDS numbering runs its region scan and its group
+    scan over more than one 512-thread round each.  Every sequence matches the oracle."""
+    T, Hq, Hkv, S = 2, 16, 2, 1100
+    lengths = [int(x) for x in np.random.default_rng(72).integers(20, 300, S)]
+    wl = W.make_gqa(72, lengths=lengths, n_new=[T] * S, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=64)
+    dev = GqaOnDevice(wl)
+    out, lse = _decode(pa_lib, dev, T)
+    got = bf16_out(out).reshape(S * T, Hq, 64)
+    lg = lse.cpu().numpy().reshape(S * T, Hq)
+    for s in range(S):
+        ro, rl = oracle.paged_gqa_attention(wl, s)
+        assert_close(got[s * T:(s + 1) * T], ro, BF16_MAX_ABS, BF16_L1, f"decode many groups seq={s}")
+        np.testing.assert_allclose(lg[s * T:(s + 1) * T], rl, atol=LSE_ABS)
+
+
 def test_decode_full_size_sampled(pa_lib):
     """The benchmarked decode workload at full size (64 sequences, 8 sessions, contexts
     4K-142K); a sample of sequences is checked against the oracle."""
