@@ -155,7 +155,8 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(GqaDecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------------
-// 2. Scan (one workgroup): region_start[r] = passes of the regions before r in region order
+// 2. Numbering (by every attention workgroup in its LDS, or past the LDS index by
+// decode_scan_kernel, one workgroup): region_start[r] = passes of the regions before r in region order
 // (the compact pass numbering; region_start[R] = P, the total), and piece_start[g] = pieces
 // before group g.  A group's regions are consecutive, so its passes are one contiguous
 // range of the numbering.  The attention grid splits [0, P) over N = min(grid, P)
@@ -262,9 +263,10 @@ __global__ __launch_bounds__(1024) void decode_scan_kernel(GqaDecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------------
-// 3. Attention: workgroup w of N = min(grid, P) takes the passes [floor(w P / N), floor((w + 1) P / N))
-// of the compact pass list -- equal shares, so the workgroups finish together -- and
-// walks them region by region (a piece per region it meets).  Each wave takes one KV
+// 3. Attention: workgroup w of N = min(grid, P) takes the passes [wg_bound(w), wg_bound(w + 1))
+// of the compact pass list -- equal shares up to the XCD skew, so the workgroups finish
+// together -- and walks them group by group (a piece per group it meets; inside a group a
+// cursor over the region starts finds each pass's slot in the plan).  Each wave takes one KV
 // head (and, when the heads are fewer than 8 and divide 8, one of 8 / Hkv equal
 // sub-ranges of the piece), so the 8 waves of a workgroup read the same blocks for all
 // heads at once (a block's K, or V, is Hkv * 4 KB contiguous) and never wait for one
