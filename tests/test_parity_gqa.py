@@ -50,13 +50,13 @@ def test_prefill_tiny_config(pa_lib):
     np.testing.assert_allclose(lse.cpu().numpy(), ref_l, atol=LSE_ABS)
 
 
-@pytest.mark.parametrize("G,D", [(1, 64), (2, 128), (4, 128), (8, 64), (4, 64)])
-def test_prefill_ragged(pa_lib, G, D):
+@pytest.mark.parametrize("G,D,Hkv", [(1, 64, 2), (2, 128, 2), (4, 128, 2), (8, 64, 2), (4, 64, 2),
+                                     (8, 128, 1), (2, 128, 16), (4, 64, 3)])
+def test_prefill_ragged(pa_lib, G, D, Hkv):
     cached = [0, 5, 1000, 33, 300]
     new = [1, 17, 130, 300, 64]
     lengths = [c + n for c, n in zip(cached, new)]
-    Hkv = 2
-    wl = W.make_gqa(30 + G + D, lengths=lengths, n_new=new, num_q_heads=Hkv * G, num_kv_heads=Hkv,
+    wl = W.make_gqa(30 + G + D + Hkv, lengths=lengths, n_new=new, num_q_heads=Hkv * G, num_kv_heads=Hkv,
                     head_dim=D)
     dev = GqaOnDevice(wl)
     out, lse = _prefill(pa_lib, dev)
@@ -65,7 +65,7 @@ def test_prefill_ragged(pa_lib, G, D):
     for s in range(wl.num_seqs):
         ro, rl = oracle.paged_gqa_attention(wl, s)
         a, b = wl.q_start[s], wl.q_start[s + 1]
-        assert_close(got[a:b], ro, BF16_MAX_ABS, BF16_L1, f"prefill G={G} D={D} seq={s}")
+        assert_close(got[a:b], ro, BF16_MAX_ABS, BF16_L1, f"prefill G={G} D={D} Hkv={Hkv} seq={s}")
         np.testing.assert_allclose(lg[a:b], rl, atol=LSE_ABS)
 
 
@@ -107,6 +107,23 @@ def test_decode_sessions(pa_lib, T, G, D, shuffle):
     for s in range(wl.num_seqs):
         ro, rl = oracle.paged_gqa_attention(wl, s)
         assert_close(got[s * T:(s + 1) * T], ro, BF16_MAX_ABS, BF16_L1, f"decode T={T} G={G} seq={s}")
+        np.testing.assert_allclose(lg[s * T:(s + 1) * T], rl, atol=LSE_ABS)
+
+
+@pytest.mark.parametrize("Hkv,G,T", [(1, 8, 1), (4, 4, 2), (16, 2, 1), (3, 4, 1)])
+def test_decode_kv_head_counts(pa_lib, Hkv, G, T):
+    """KV head counts other than 2 and 8: one head split over all 8 waves (8 sub-ranges of
+    each piece), 4 heads x 2 sub-ranges, 16 heads (two per wave) and 3 heads (8 does not
+    divide: one sub-range, waves 3-7 idle); sessions share 90 % of their blocks."""
+    wl = W.make_gqa_decode(80 + Hkv, n_sessions=3, members=4, lo=30, hi=4000, q_per_seq=T,
+                           num_q_heads=Hkv * G, num_kv_heads=Hkv, head_dim=128, keep_content=True)
+    dev = GqaOnDevice(wl)
+    out, lse = _decode(pa_lib, dev, T)
+    got = bf16_out(out).reshape(wl.num_seqs * T, wl.num_q_heads, 128)
+    lg = lse.cpu().numpy().reshape(wl.num_seqs * T, wl.num_q_heads)
+    for s in range(wl.num_seqs):
+        ro, rl = oracle.paged_gqa_attention(wl, s)
+        assert_close(got[s * T:(s + 1) * T], ro, BF16_MAX_ABS, BF16_L1, f"decode Hkv={Hkv} G={G} T={T} seq={s}")
         np.testing.assert_allclose(lg[s * T:(s + 1) * T], rl, atol=LSE_ABS)
 
 
