@@ -48,7 +48,7 @@ def test_gather_fp8_bit_exact(pa_lib):
         assert np.array_equal(k.cpu().numpy(), c) and np.array_equal(sc.cpu().numpy(), cs)
 
 
-@pytest.mark.parametrize("T,Hq", [(4, 64), (1, 64), (4, 16), (2, 32)])
+@pytest.mark.parametrize("T,Hq", [(4, 64), (1, 64), (4, 16), (2, 32), (3, 128), (1, 16)])
 def test_mla_decode(pa_lib, T, Hq):
     lengths = [T, 63, 64, 65, 3000, 8192 + 100, 17000]
     mla = W.make_mla_decode(72 + T, lengths=lengths, q_per_seq=T, num_q_heads=Hq)
@@ -207,14 +207,15 @@ def test_sparse_mla_k_covers_context_equals_dense(pa_lib):
     assert_close(bf16_out(out), ro, FP8_MAX_ABS, FP8_L1, "sparse == dense")
 
 
-@pytest.mark.parametrize("k", [100, 2500])
-def test_sparse_mla_given_selection(pa_lib, k):
+@pytest.mark.parametrize("k,Hq", [(100, 64), (2500, 64), (300, 16), (300, 128)])
+def test_sparse_mla_given_selection(pa_lib, k, Hq):
     """Selections handed in directly, in random order with -1 holes: k <= 2,048 takes the
     path with the selections' rows staged in LDS, k > 2,048 the one that resolves each
-    tile's rows from global memory.  A row with no selection at all gives zeros."""
+    tile's rows from global memory; 16 heads leave half of each wave's rows empty, 128
+    heads take two workgroups per query.  A row with no selection at all gives zeros."""
     import torch
     n = 24
-    mla, idx = W.make_sparse_mla(93, lengths=[3000 + n], n_new=[n], num_q_heads=64)
+    mla, idx = W.make_sparse_mla(93, lengths=[3000 + n], n_new=[n], num_q_heads=Hq)
     dev = MlaOnDevice(mla, idx)
     rng = np.random.default_rng(1000 + k)
     pos = mla.q_pos(0)
@@ -231,7 +232,7 @@ def test_sparse_mla_given_selection(pa_lib, k):
     codes = oracle.gather_paged(mla.kv_pool, mla.block_table[0], L)
     sc = oracle.gather_paged(mla.kv_scale[..., None], mla.block_table[0], L)[:, 0]
     ro, _ = oracle.sparse_mla_attention(mla.q[0:n], codes, sc, tk, mla.scale)
-    assert_close(got, ro, FP8_MAX_ABS, FP8_L1, f"sparse given selection k={k}")
+    assert_close(got, ro, FP8_MAX_ABS, FP8_L1, f"sparse given selection k={k} Hq={Hq}")
     assert np.all(got[n - 1] == 0)
 
 
