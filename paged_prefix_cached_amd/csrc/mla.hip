@@ -449,15 +449,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 #pragma unroll
   for (int w = 0; w < NW; ++w) overflow |= ovf_s[w] != 0;
 
-  // ---- finish: full row sum over the two lane halves, write the 32 rows x 512 dims
+  // ---- finish: full row sum over the two lane halves, write the 32 rows x 512 dims.  The
+  // lane's row and half are derived again here (from the lane id, counted with mbcnt) rather
+  // than kept in registers through the tile loop.
   const float l_tot = halves_sum(l_run);
-  if (!row_ok) return;
+  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int row_e = row0 + wave * 32 + (lane_e & 31), h_e = lane_e >> 5;
+  if (row_e >= rows_total) return;
   if (overflow) {
     // mark the unit for the exact recomputation: a NaN in every row's LSE (decode) or in
     // the first output element of every row (sparse)
-    if (h == 0) {
-      if constexpr (SPARSE) sa.out[((size_t)unit * Hq + row) * kDv] = 0x7fc1;
-      else da.part_lse[((size_t)unit * da.max_splits + unit_split) * rows_total + row] = __builtin_nanf("");
+    if (h_e == 0) {
+      if constexpr (SPARSE) sa.out[((size_t)unit * Hq + row_e) * kDv] = 0x7fc1;
+      else da.part_lse[((size_t)unit * da.max_splits + unit_split) * rows_total + row_e] = __builtin_nanf("");
     }
     return;
   }
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   const float lse2 = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
   // acc[mt][4 q + i] = O[row][32 mt + 8 q + 4 h + i]
   if constexpr (SPARSE) {
-    uint16_t* op = sa.out + ((size_t)unit * Hq + row) * kDv + 4 * h;
+    uint16_t* op = sa.out + ((size_t)unit * Hq + row_e) * kDv + 4 * h_e;
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
@@ -475,17 +479,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
         w.y = pack_bf16x2(acc[mt][4 * q + 2] * inv, acc[mt][4 * q + 3] * inv);
         *reinterpret_cast<u32x2*>(op + 32 * mt + 8 * q) = w;
       }
-    if (sa.lse != nullptr && h == 0) sa.lse[(size_t)unit * Hq + row] = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
+    if (sa.lse != nullptr && h_e == 0) sa.lse[(size_t)unit * Hq + row_e] = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
   } else {
-    const size_t pbase = ((size_t)unit * da.max_splits + unit_split) * rows_total + row;
-    float* op = da.part_o + pbase * kDv + 4 * h;
+    const size_t pbase = ((size_t)unit * da.max_splits + unit_split) * rows_total + row_e;
+    float* op = da.part_o + pbase * kDv + 4 * h_e;
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<f32x4*>(op + 32 * mt + 8 * q) =
             f32x4{acc[mt][4 * q], acc[mt][4 * q + 1], acc[mt][4 * q + 2], acc[mt][4 * q + 3]} * inv;
-    if (h == 0) da.part_lse[pbase] = lse2;
+    if (h_e == 0) da.part_lse[pbase] = lse2;
   }
 }
 
