@@ -139,3 +139,41 @@ def test_random_sparse_mla(pa_lib, seed):
     sc = oracle.gather_paged(mla.kv_scale[..., None], mla.block_table[0], L)[:, 0]
     ro, _ = oracle.sparse_mla_attention(mla.q[0:n], codes, sc, tk, mla.scale)
     assert_close(bf16_out(out), ro, FP8_MAX_ABS, FP8_L1, f"sparse seed={seed} Hq={Hq} n={n} k={k} L={L}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_indexer_topk(pa_lib, seed):
+    """Indexer scores against the oracle (relative bound as in the fixed-shape test) and the
+    top-k index sets bit-exact against the oracle's top-k on the kernel's own scores, for a
+    random batch of sequences, head counts and k (including k above some rows' counts)."""
+    import torch
+    rng = np.random.default_rng(1300 + seed)
+    S = int(rng.integers(1, 4))
+    H = int(rng.choice([16, 32, 48, 64]))
+    k = int(rng.choice([1, 33, 256, 2048]))
+    n_new = [int(x) for x in _lengths(rng, S, 1, 60)]
+    cached = [int(x) for x in rng.integers(0, 9000, S)]
+    lengths = [c + n for c, n in zip(cached, n_new)]
+    mla, idx = W.make_sparse_mla(1350 + seed, lengths=lengths, n_new=n_new, num_q_heads=16, idx_heads=H)
+    dev = MlaOnDevice(mla, idx)
+    n_q = dev.q_idx.shape[0]
+    scores = torch.empty((n_q, dev.max_total), dtype=torch.float32, device="cuda")
+    topk = pa_lib.mla_indexer_topk(dev.q_idx, dev.w, dev.idx_pool, dev.bt, dev.cached, dev.n_new, dev.q_start,
+                                   max_new_len=dev.max_new, max_total_len=dev.max_total, k=k, scores_out=scores)
+    torch.cuda.synchronize()
+    topk = topk.cpu().numpy()
+    sc = scores.cpu().numpy().astype(np.float64)
+    for s in range(S):
+        L = int(mla.total_len[s])
+        kc = oracle.gather_paged(idx.idx_pool, mla.block_table[s], L)
+        ks = oracle.gather_paged(idx.idx_scale[..., None], mla.block_table[s], L)[:, 0]
+        a, b = mla.q_start[s], mla.q_start[s + 1]
+        pos = mla.q_pos(s)
+        ref = oracle.indexer_scores(idx.q_idx[a:b], idx.w[a:b], kc, ks, pos)
+        got = sc[a:b, :L]
+        fin = np.isfinite(ref)
+        assert np.array_equal(fin, np.isfinite(got)), (seed, s)
+        err = np.abs(got[fin] - ref[fin])
+        assert err.max() <= 2e-3 * np.abs(ref[fin]).max(), (seed, s, err.max())
+        for r in range(b - a):
+            assert np.array_equal(topk[a + r], oracle.topk_indices(got[r], pos[r] + 1, k)), (seed, s, r)
