@@ -196,3 +196,21 @@ def test_append_fp8_sparse_prefill_full_size(pa_lib, D):
     """The sparse-MLA workload's new tokens: 4096 rows after 131072 cached (latent and
     indexer keys)."""
     _full_size_fp8(pa_lib, [131072], [4096], D, 72 + D)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_append_random_shapes(pa_lib, seed):
+    """Random batches of (cached, new) pairs, bf16 rows of random head counts and dims and
+    FP8 rows of both widths; the whole pool is compared bit for bit each time."""
+    rng = np.random.default_rng(1500 + seed)
+    S = int(rng.integers(1, 9))
+    cached = [int(x) for x in rng.integers(0, 700, S)]
+    new = [int(x) for x in rng.integers(0, 90, S)]
+    hkv, d = int(rng.choice([1, 2, 4, 8])), int(rng.choice([64, 128]))
+    a = W.make_append(1550 + seed, cached=cached, new=new, block_size=16, row_shape=(hkv, d), with_v=True)
+    if a.k_new.shape[0] > 0:
+        _run_gqa(pa_lib, a, hkv, d, 1600 + seed)
+    D = int(rng.choice([576, 128]))
+    f = W.make_append(1650 + seed, cached=cached, new=new, block_size=64, row_shape=(D,), with_v=False)
+    if f.k_new.shape[0] > 0:
+        _run_fp8(pa_lib, f, D, 1700 + seed)
