@@ -59,6 +59,7 @@ constexpr int kTileLoads = kTileB / 1024;    // 18 wave-loads of 1 KB (two chunk
 constexpr int kQS = kDqk / 16;               // 36 Q.K k-steps
 constexpr int kMT = kDv / 32;                // 16 output tiles of 32 dims
 constexpr int kSelLds = 2048;                // sparse selections staged in LDS
+constexpr uint32_t kNoRow = 0xffffff;        // staged row (24 bits) of an unread selection
 constexpr float kSlack = 8.f;                // log2 units: probabilities stay <= 2^8
 constexpr int kPre = 8;                      // LDS fragment reads in flight ahead of use
 
@@ -104,7 +105,8 @@ __device__ __forceinline__ void wait_vm_upto(int n) {
 }
 
 // NW waves (NW x 32 query rows) per workgroup, one wave per SIMD; NBUF tile buffers.
-// STAGED (sparse): the selections' physical rows (k <= 2048) are staged in LDS once;
+// STAGED (sparse): the selections' physical rows (k <= 2048, rows below 2^24 - 1) are staged
+// in LDS once, 3 bytes each (6 KB: two workgroups of 4 tile buffers then fit on a CU);
 // otherwise each tile resolves them from global memory.
 template <bool SPARSE, int NW, int NBUF, bool STAGED>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void mla_kernel(MlaDecodeArgs da,
@@ -122,7 +124,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   constexpr bool kFiller = NW * kLoadsMax != kTileLoads;           // some waves have a spare load
   __shared__ __attribute__((aligned(16))) uint8_t spare[kFiller ? 1024 : 16];  // its target
   __shared__ int32_t bt_s[SPARSE ? 1 : kDecodeSplitMla / kBs + 1];
-  __shared__ int32_t sel_s[SPARSE && STAGED ? kSelLds : 1];
+  __shared__ uint16_t sel_lo[SPARSE && STAGED ? kSelLds : 1];     // staged rows: bits 0-15
+  __shared__ uint8_t sel_hi[SPARSE && STAGED ? kSelLds : 1];      // and bits 16-23
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -211,7 +214,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   };
   if constexpr (SPARSE) {
     if constexpr (STAGED)
-      for (int j = tid; j < n_keys; j += NT) sel_s[j] = sel_row(sel_g[j]);
+      for (int j = tid; j < n_keys; j += NT) {
+        const uint32_t r = (uint32_t)sel_row(sel_g[j]) & kNoRow;   // -1 -> kNoRow
+        sel_lo[j] = (uint16_t)r;
+        sel_hi[j] = (uint8_t)(r >> 16);
+      }
   } else {
     for (int j = tid; j < n_bt; j += NT) bt_s[j] = phys_block(bt_row, lb_base + j, n_lblocks, num_blocks);
   }
@@ -244,8 +251,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
       const int j = kb + dma_key;
       int q = -1;
       if (j < n_keys) {
-        if constexpr (STAGED) q = sel_s[j];
-        else q = sel_row(sel_g[j]);
+        if constexpr (STAGED) {
+          const uint32_t r = sel_lo[j] | ((uint32_t)sel_hi[j] << 16);
+          q = r == kNoRow ? -1 : (int)r;
+        } else {
+          q = sel_row(sel_g[j]);
+        }
       }
       valid = q >= 0;
       const size_t qb = (size_t)(uint32_t)max(q, 0);
@@ -497,7 +508,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 #define PA_MLA2_DECODE_NBUF 4
 #endif
 #ifndef PA_MLA2_SPARSE_NBUF
-#define PA_MLA2_SPARSE_NBUF 3
+#define PA_MLA2_SPARSE_NBUF 4
 #endif
 constexpr int kDecWaves = 4, kSpWaves = 2;
 constexpr int kDecBuf = PA_MLA2_DECODE_NBUF, kSpBuf = PA_MLA2_SPARSE_NBUF;
@@ -519,7 +530,7 @@ hipError_t launch_sparse_mla(const SparseMlaArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)a.n_q * ((a.num_q_heads + 32 * kSpWaves - 1) / (32 * kSpWaves));
   if (grid == 0) return hipSuccess;
   MlaDecodeArgs none{};
-  if (a.k <= kSelLds)
+  if (a.k <= kSelLds && (int64_t)a.num_blocks * kBs < (int64_t)kNoRow)
     hipLaunchKernelGGL((mla_kernel<true, kSpWaves, kSpBuf, true>), dim3(grid), dim3(64 * kSpWaves), 0, stream, none, a);
   else
     hipLaunchKernelGGL((mla_kernel<true, kSpWaves, kSpBuf, false>), dim3(grid), dim3(64 * kSpWaves), 0, stream, none, a);
