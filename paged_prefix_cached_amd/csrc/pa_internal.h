@@ -9,7 +9,7 @@ namespace pa {
 // MLA decode: keys per split of the key range.  Each split yields a partial (o, lse) pair
 // that the combine kernel merges in split order.
 #ifndef PA_DECODE_SPLIT_MLA
-#define PA_DECODE_SPLIT_MLA 4096
+#define PA_DECODE_SPLIT_MLA 6144
 #endif
 constexpr int kDecodeSplitMla = PA_DECODE_SPLIT_MLA;
 

@@ -56,7 +56,7 @@ def test_suffix_prefill_full_size_sampled(pa_lib):
 
 def test_mla_mtp3_decode_full_size_sampled(pa_lib):
     """64 sequences x 4 MTP tokens, 64 heads, FP8 latent, contexts U[32768, 262144]: the
-    shortest, median and longest sequences (all 4 tokens x 64 heads, up to 64 splits)."""
+    shortest, median and longest sequences (all 4 tokens x 64 heads, up to 43 splits)."""
     import torch
     t0 = time.time()
     mla = W.make_mla_decode(4)

@@ -253,13 +253,13 @@ def _tile_overflow(scores_log2: np.ndarray, tile: int = 32, slack: float = 8.0) 
 
 
 def test_mla_decode_fixed_reference_fallback(pa_lib):
-    """Moderately peaked queries: in some work units (4,096 keys x 128 query rows) a row's
+    """Moderately peaked queries: in some work units (6,144 keys x 128 query rows) a row's
     maximum climbs far above its first tile's, so the fixed-reference kernel marks the unit
     and the exact kernel recomputes it; the other units stay on the fast path.  Both kinds
     are in this call and every row matches the oracle."""
     T, Hq = 4, 64
     lengths = [5000, 20000]
-    mla = W.make_mla_decode(79, lengths=lengths, q_per_seq=T, num_q_heads=Hq, q_mult=2.0)
+    mla = W.make_mla_decode(79, lengths=lengths, q_per_seq=T, num_q_heads=Hq, q_mult=1.8)
     n_over = n_units = 0
     for s in range(len(lengths)):
         L = lengths[s]
@@ -270,8 +270,8 @@ def test_mla_decode_fixed_reference_fallback(pa_lib):
         pos = np.repeat(mla.q_pos(s), Hq)
         sl = (q @ k.T) * (mla.scale / np.log(2.0))
         sl[np.arange(L)[None, :] > pos[:, None]] = -np.inf
-        for k0 in range(0, L, 4096):
-            ov = _tile_overflow(sl[:, k0:k0 + 4096]).reshape(2, 128)    # two 128-row units
+        for k0 in range(0, L, 6144):
+            ov = _tile_overflow(sl[:, k0:k0 + 6144]).reshape(2, 128)    # two 128-row units
             n_units += 2
             n_over += int(ov.any(axis=1).sum())
     assert 0 < n_over < n_units, (n_over, n_units)
