@@ -236,6 +236,50 @@ def test_sparse_mla_given_selection(pa_lib, k, Hq):
     assert np.all(got[n - 1] == 0)
 
 
+@pytest.mark.parametrize("num_blocks", [262143, 262144])
+def test_sparse_mla_rows_near_2_24(pa_lib, num_blocks):
+    """The staged path keeps each selection's physical row (block x 64 + slot) in 24 bits,
+    0xffffff marking a hole: a pool of 262,143 blocks has rows up to 0xffffbf and is staged;
+    one more block (rows up to 0xffffff) makes the call resolve the rows per tile from global
+    memory instead.  The workload's blocks sit at the highest block ids of such a pool (every
+    other id from the top; the rest of the pool is never read) and every row must match the
+    oracle on the original layout."""
+    import torch
+    import paged_prefix_cached_amd as pa
+    n, k, Hq = 8, 300, 64
+    mla, idx = W.make_sparse_mla(95, lengths=[900 + n], n_new=[n], num_q_heads=Hq)
+    dev = MlaOnDevice(mla, idx)
+    L = int(mla.total_len[0])
+    nlb = -(-L // 64)
+    old_ids = mla.block_table[0, :nlb].astype(np.int64)
+    new_ids = num_blocks - 1 - 2 * np.arange(nlb)
+    kv = torch.empty((num_blocks, 64, 576), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((num_blocks, 64), dtype=torch.float32, device="cuda")
+    dst = torch.from_numpy(new_ids).cuda()
+    kv[dst] = torch.from_numpy(mla.kv_pool[old_ids]).cuda()
+    ks[dst] = torch.from_numpy(mla.kv_scale[old_ids]).cuda()
+    pool = pa.mla_pool(kv, ks)
+    bt = mla.block_table.copy()
+    bt[0, :nlb] = new_ids
+    rng = np.random.default_rng(95)
+    pos = mla.q_pos(0)
+    tk = np.full((n, k), -1, np.int32)
+    for r in range(n):
+        m = min(k, int(pos[r]) + 1) - int(rng.integers(0, 7))
+        tk[r, :m] = rng.choice(int(pos[r]) + 1, size=m, replace=False)
+        tk[r] = rng.permutation(tk[r])
+    out = pa_lib.sparse_mla_attn(dev.q, pool, torch.from_numpy(bt).cuda(), dev.q_seq, torch.from_numpy(tk).cuda(),
+                                 scale=mla.scale)
+    torch.cuda.synchronize()
+    got = bf16_out(out)
+    del kv, ks, pool
+    torch.cuda.empty_cache()
+    codes = oracle.gather_paged(mla.kv_pool, mla.block_table[0], L)
+    sc = oracle.gather_paged(mla.kv_scale[..., None], mla.block_table[0], L)[:, 0]
+    ro, _ = oracle.sparse_mla_attention(mla.q[0:n], codes, sc, tk, mla.scale)
+    assert_close(got, ro, FP8_MAX_ABS, FP8_L1, f"sparse rows near 2^24, {num_blocks} blocks")
+
+
 def _tile_overflow(scores_log2: np.ndarray, tile: int = 32, slack: float = 8.0) -> np.ndarray:
     """Per row of scores (log2 units, -inf = masked, in the kernel's key order): whether the
     MLA kernel's fixed reference (the row maximum of the first tile holding a visible key)
