@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the paged, prefix-reused attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--secondary 3,4,5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--secondary 2n,3,4,5,5p] [--no-cpu-baseline]
 
 A step is one paged_attn_decode call over the decode batch: 64 sequences x 1 query
 token, 32 query / 8 KV heads, head dim 128, bf16 K/V in a shuffled 16-token block pool,
@@ -22,8 +22,9 @@ sequence's whole context instead (shared prefix blocks once per sequence).  The 
 object uses the same algorithmic bytes over the decode kernel's average launch time.
 `cpu_baseline` times the CPU oracle (oracle/) on the same batch with a process pool over
 the sequences, one single-threaded process per host core.  `secondary` holds the other
-workloads (suffix prefill, MLA MTP3 decode, indexer + top-k + sparse MLA on separate pools
-and on the packed per-block layout with MXFP4 index keys, by default).
+workloads (by default: the same decode batch with no shared blocks as a control, suffix
+prefill, MLA MTP3 decode, indexer + top-k + sparse MLA on separate pools and on the packed
+per-block layout with MXFP4 index keys).
 """
 from __future__ import annotations
 
@@ -597,8 +598,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--secondary", default="3,4,5,5p",
-                    help="comma list of extra workloads (default 3,4,5,5p; '' for none): 2n (decode with no "
+    ap.add_argument("--secondary", default="2n,3,4,5,5p",
+                    help="comma list of extra workloads (default 2n,3,4,5,5p; '' for none): 2n (decode with no "
                          "shared blocks), 3 (suffix prefill), 4 (MLA MTP3 decode), 5 (indexer + top-k + "
                          "sparse MLA), 5p (the same on the packed layout with MXFP4 index keys), a (KV append), "
                          "c (cold-prompt prefill), m (chunked-prefill step)")
