@@ -7,15 +7,29 @@
 // is a known hotspot).
 //
 // Scores are compared through order-preserving 32-bit keys (-0.0 keyed as +0.0, so the
-// two zeros tie).  One workgroup of 1,024 threads per row; the row is read twice:
+// two zeros tie).  One workgroup of 1,024 threads per row.
+//
+// One read (rows of at least kOneReadMin tokens, k <= kCand / 4): a sample of 4,096
+// scores from 16 evenly spaced runs of the row gives, by a two-level LDS histogram, a key
+// threshold tau that about 2k of the row's keys reach.  The row is then read once; every
+// key >= tau is appended (key, token) to an LDS candidate list, each wave reserving its
+// slots with one LDS atomic per 16,384-score step, so the pass has no barrier.  If at
+// least k and at most kCand keys reached tau, the list holds the whole top k (the k-th
+// largest key of the row is >= tau); a radix select over the list finds T, the k-th
+// largest key, and how many keys equal to T to take; the taken ties (lowest tokens first,
+// through an index-ordered scan of an LDS bitmap) and the keys above T set their bits in
+// the bitmap, and a prefix sum over its popcounts writes the tokens in ascending order.
+// Otherwise (the sample misled: too few or too many keys reached tau) the row takes the
+// two-read path below.
+//
+// Two reads (shorter rows, and the fallback):
 //   1. a 4,096-bin LDS histogram of the top 12 key bits locates the bin b holding the
 //      k-th largest key, with G keys above it;
-//   2. in index order, keys above b set their bit in an LDS selection bitmap and keys in
-//      b are appended, in index order, to an LDS candidate list;
-// then, in LDS only: a radix select over the candidates' low 20 bits finds T, the k-th
-// largest key, and how many keys equal to T to take; candidates above T and the first
-// such ties (in index order) join the bitmap; a prefix sum over bitmap popcounts writes
-// the selected indices in ascending order.
+//   2. in index order, keys above b set their bit in the bitmap and keys in b are
+//      appended, in index order, to the candidate list;
+// then, in LDS only: a radix select over the candidates' low 20 bits finds T and the
+// number of ties to take; candidates above T and the first such ties (in index order)
+// join the bitmap, which is compacted as above.
 // Rows longer than the bitmap or whose bin b overflows the candidate list fall back to
 // four 8-bit radix passes over the row plus an index-ordered compaction pass.
 #include "pa_device.h"
@@ -29,8 +43,15 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 4096;                 // top 12 key bits
 constexpr int kMaxBits = 1 << 18;           // bitmap capacity (tokens per row)
 constexpr int kWords = kMaxBits / 32;
-constexpr int kCand = 3072;                 // candidate list capacity
+constexpr int kCand = 8192;                 // candidate list capacity
+constexpr int kSampleRun = 256;             // sample: one run of 256 scores per wave (4 a lane)
+constexpr int kSample = kWaves * kSampleRun;  // 4,096 sampled scores
+constexpr int kOneReadMin = 32768;          // shortest row that tries the one-read path
+constexpr int kMinRank = 64;                // smallest sample rank used for the threshold
+constexpr int kPer = 16;                    // scores per thread and step
+constexpr int kSuper = kThreads * kPer;     // scores per workgroup step
 static_assert(kBins <= 4 * kThreads, "bin search covers 4 bins a thread");
+static_assert(kOneReadMin / kWaves >= kSampleRun, "sample runs do not overlap");
 
 __device__ __forceinline__ uint32_t score_key(float f) {
   const uint32_t u = __float_as_uint(f + 0.0f);
@@ -51,6 +72,10 @@ __device__ __forceinline__ void load16(const float* sc, int e0, int valid, float
 #pragma unroll
     for (int j = 0; j < 16; ++j) f[j] = e0 + j < valid ? sc[e0 + j] : 0.f;
   }
+}
+
+__device__ __forceinline__ void load16v(bool vec, const float* sc, int e0, int valid, float (&f)[16]) {
+  if (vec) load16<true>(sc, e0, valid, f); else load16<false>(sc, e0, valid, f);
 }
 
 // Exclusive prefix sum over the workgroup; returns the exclusive value, sets total.
@@ -83,12 +108,13 @@ struct TopkSmem {
   uint32_t ckey[kCand];
   int wsum[kWaves];
   uint32_t sh_bin, sh_kk, sh_n;
+  int n_cand;
 };
 
 // Bin d of sm.hist[0..nbins) (nbins a multiple of 4, at most 4 * kThreads) with G keys in
 // the bins above it and G < kk <= G + hist[d]: d -> sm.sh_bin, kk - G -> sm.sh_kk,
 // hist[d] -> sm.sh_n.  Each thread sums a group of 4 bins; a block scan in reversed
-// group order gives the count above every group.
+// group order gives the count above every group.  The caller guarantees kk <= the total.
 __device__ void find_bin_from_top(TopkSmem& sm, int nbins, uint32_t kk) {
   const int g = nbins / 4 - 1 - (int)threadIdx.x;
   uint32_t c[4] = {0u, 0u, 0u, 0u};
@@ -110,16 +136,17 @@ __device__ void find_bin_from_top(TopkSmem& sm, int nbins, uint32_t kk) {
   __syncthreads();
 }
 
-// Radix select on a prefix-filtered set held in the candidate list: the kk-th largest key
-// among ckey[0..n) (all sharing the top 12 bits), as T and the number of keys equal to T
-// that are taken.  Two passes over bits 19..8 (12 bits) and 7..0 (8 bits).
-__device__ void select_in_candidates(TopkSmem& sm, int n, uint32_t kk, uint32_t& T, uint32_t& kk_eq) {
+// Radix select in LDS: the kk-th largest key among ckey[0..n) whose bits under `mask` equal
+// `prefix`, over the key fields from `first` on (bits 31..20, 19..8, 7..0).  Returns T,
+// the number of keys equal to T that are taken (kk_eq) and the number of keys equal to T
+// among the filtered ones (n_eq).
+__device__ void select_kth(TopkSmem& sm, int n, uint32_t kk, int first, uint32_t prefix, uint32_t mask,
+                           uint32_t& T, uint32_t& kk_eq, uint32_t& n_eq) {
   const int tid = threadIdx.x;
-  uint32_t prefix = sm.ckey[0] & 0xFFF00000u, mask = 0xFFF00000u;
-  const int shifts[2] = {8, 0};
-  const int widths[2] = {12, 8};
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
+  const int shifts[3] = {20, 8, 0};
+  const int widths[3] = {12, 12, 8};
+  uint32_t cnt = 0;
+  for (int pass = first; pass < 3; ++pass) {
     const int sh = shifts[pass], nb = 1 << widths[pass];
     for (int j = tid; j < nb; j += kThreads) sm.hist[j] = 0u;
     __syncthreads();
@@ -131,11 +158,34 @@ __device__ void select_in_candidates(TopkSmem& sm, int n, uint32_t kk, uint32_t&
     find_bin_from_top(sm, nb, kk);
     prefix |= sm.sh_bin << sh;
     kk = sm.sh_kk;
+    cnt = sm.sh_n;
     mask |= (uint32_t)(nb - 1) << sh;
     __syncthreads();
   }
   T = prefix;
   kk_eq = kk;
+  n_eq = cnt;
+}
+
+// The bitmap's set bits, in ascending token order, to out[0..k): each thread owns a run
+// of consecutive words.
+__device__ void write_bitmap(TopkSmem& sm, int nwords, int k, int32_t* out) {
+  const int tid = threadIdx.x;
+  const int per = (nwords + kThreads - 1) / kThreads;
+  const int w_begin = min(nwords, tid * per), w_end = min(nwords, w_begin + per);
+  int cnt = 0;
+  for (int w = w_begin; w < w_end; ++w) cnt += __popc(sm.bits[w]);
+  int tot;
+  int slot = block_excl_scan(cnt, sm.wsum, tot);
+  for (int w = w_begin; w < w_end; ++w) {
+    uint32_t x = sm.bits[w];
+    while (x != 0u) {
+      const int bit = __ffs(x) - 1;
+      x &= x - 1u;
+      if (slot < k) out[slot] = 32 * w + bit;
+      ++slot;
+    }
+  }
 }
 
 // Fallback: four 8-bit radix passes over the row, then an index-ordered compaction.
@@ -175,28 +225,130 @@ __device__ void topk_radix_row(TopkSmem& sm, const float* sc, int valid, int k, 
   }
 }
 
-__global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
-  __shared__ TopkSmem sm;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int row = blockIdx.x;
-  const int valid = max(0, min(a.valid_len[row], a.max_valid));
-  const int k = a.k;
-  int32_t* out = a.out + (size_t)row * k;
-  const float* sc = a.scores + (size_t)row * a.row_stride;
-  if (valid <= k) {
-    for (int j = tid; j < k; j += kThreads) out[j] = j < valid ? j : -1;
-    return;
-  }
-  if (valid > kMaxBits) {
-    topk_radix_row(sm, sc, valid, k, out);
-    return;
-  }
+// One read of the row (see the file comment).  Returns false, uniformly over the
+// workgroup and with nothing written to out, when the sampled threshold did not leave
+// between k and kCand candidates; the caller then runs the two-read path.
+// Requires kOneReadMin <= valid <= kMaxBits and k <= kCand / 4.
+__device__ bool topk_one_read(TopkSmem& sm, const float* sc, int valid, int k, int32_t* out, bool vec) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_super = (valid + kSuper - 1) / kSuper;
+  // The first step's loads go out before the sample is processed.
+  float cur[kPer], nxt[kPer];
+  load16v(vec, sc, kPer * tid, valid, cur);
 
-  // Both passes walk the row in super-chunks of 16 consecutive scores per thread
-  // (16,384 per workgroup step), the next super-chunk's loads in flight while the current
-  // one is processed.
-  constexpr int kPer = 16, kSuper = kThreads * kPer;
-  const bool vec = ((reinterpret_cast<uintptr_t>(sc) & 15u) == 0);
+  // ---- sample: run w (wave w) starts at w (valid - 256) / 15, rounded down to 4 scores
+  const int r0 = (int)(((long long)wave * (valid - kSampleRun) / (kWaves - 1)) & ~3ll);
+  uint32_t skey[4];
+  if (vec) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(sc + r0 + 4 * lane);
+    skey[0] = score_key(v.x); skey[1] = score_key(v.y); skey[2] = score_key(v.z); skey[3] = score_key(v.w);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) skey[i] = score_key(sc[r0 + 4 * lane + i]);
+  }
+  for (int j = tid; j < kBins; j += kThreads) sm.hist[j] = 0u;
+  if (tid == 0) sm.n_cand = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) atomicAdd(&sm.hist[skey[i] >> 20], 1u);
+  __syncthreads();
+  // rank in the sample whose key about 2k of the row's keys reach (at least kMinRank, so
+  // that the count stays close to its expectation)
+  const int want = (int)(((long long)2 * k * kSample + valid - 1) / valid);
+  const uint32_t rank = (uint32_t)min(kSample, max(kMinRank, want));
+  find_bin_from_top(sm, kBins, rank);
+  const uint32_t b12 = sm.sh_bin, rr = sm.sh_kk;
+  for (int j = tid; j < 256; j += kThreads) sm.hist[j] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if ((skey[i] >> 20) == b12) atomicAdd(&sm.hist[(skey[i] >> 12) & 255u], 1u);
+  __syncthreads();
+  find_bin_from_top(sm, 256, rr);
+  const uint32_t tau = (b12 << 20) | (sm.sh_bin << 12);
+
+  // ---- the row, once: keys >= tau to the candidate list (slots reserved per wave)
+  for (int sI = 0; sI < n_super; ++sI) {
+    const int e0 = sI * kSuper + kPer * tid;
+    if (sI + 1 < n_super) load16v(vec, sc, e0 + kSuper, valid, nxt);
+    uint32_t accm = 0u;                                // bit j: score j reaches tau
+    int tot = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const bool acc = e0 + j < valid && score_key(cur[j]) >= tau;
+      accm |= acc ? (1u << j) : 0u;
+      tot += __popcll(__ballot(acc));
+    }
+    if (tot > 0) {                                     // wave-uniform
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&sm.n_cand, tot);
+      int slot = __shfl(base, 0);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const bool acc = (accm >> j) & 1u;
+        const uint64_t bal = __ballot(acc);
+        if (acc) {
+          const int s_j = slot + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+          if (s_j < kCand) {
+            sm.ckey[s_j] = score_key(cur[j]);
+            sm.cidx[s_j] = e0 + j;
+          }
+        }
+        slot += __popcll(bal);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) cur[j] = nxt[j];
+  }
+  __syncthreads();
+  const int n = sm.n_cand;
+  if (n < k || n > kCand) return false;
+
+  // ---- T, the k-th largest key among the candidates, and the ties to take
+  uint32_t T, kk_eq, n_eq;
+  select_kth(sm, n, (uint32_t)k, 0, 0u, 0u, T, kk_eq, n_eq);
+  const int nwords = (valid + 31) / 32;
+  for (int j = tid; j < nwords; j += kThreads) sm.bits[j] = 0u;
+  __syncthreads();
+  if (n_eq != kk_eq) {
+    // more keys equal T than are taken: keep the kk_eq lowest tokens among them
+    for (int i = tid; i < n; i += kThreads)
+      if (sm.ckey[i] == T) atomicOr(&sm.bits[sm.cidx[i] >> 5], 1u << (sm.cidx[i] & 31));
+    __syncthreads();
+    const int per = (nwords + kThreads - 1) / kThreads;
+    const int w_begin = min(nwords, tid * per), w_end = min(nwords, w_begin + per);
+    int cnt = 0;
+    for (int w = w_begin; w < w_end; ++w) cnt += __popc(sm.bits[w]);
+    int tot;
+    int rank_t = block_excl_scan(cnt, sm.wsum, tot);
+    for (int w = w_begin; w < w_end; ++w) {
+      uint32_t x = sm.bits[w], keep = 0u;
+      while (x != 0u) {
+        const uint32_t low = x & (0u - x);
+        x ^= low;
+        if (rank_t < (int)kk_eq) keep |= low;
+        ++rank_t;
+      }
+      sm.bits[w] = keep;
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += kThreads)
+      if (sm.ckey[i] > T) atomicOr(&sm.bits[sm.cidx[i] >> 5], 1u << (sm.cidx[i] & 31));
+  } else {
+    for (int i = tid; i < n; i += kThreads)
+      if (sm.ckey[i] >= T) atomicOr(&sm.bits[sm.cidx[i] >> 5], 1u << (sm.cidx[i] & 31));
+  }
+  __syncthreads();
+  write_bitmap(sm, nwords, k, out);
+  return true;
+}
+
+// Two reads of the row (see the file comment).  Requires k < valid <= kMaxBits.
+__device__ void topk_two_reads(TopkSmem& sm, const float* sc, int valid, int k, int32_t* out, bool vec) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  // Both passes walk the row in steps of 16 consecutive scores per thread (16,384 per
+  // workgroup step), the next step's loads in flight while the current one is processed.
   const int n_super = (valid + kSuper - 1) / kSuper;
 
   // ---- pass 1: histogram of the top 12 key bits
@@ -204,12 +356,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   __syncthreads();
   {
     float cur[kPer], nxt[kPer];
-    if (vec) load16<true>(sc, kPer * tid, valid, cur); else load16<false>(sc, kPer * tid, valid, cur);
+    load16v(vec, sc, kPer * tid, valid, cur);
     for (int sI = 0; sI < n_super; ++sI) {
       const int e0 = sI * kSuper + kPer * tid;
-      if (sI + 1 < n_super) {
-        if (vec) load16<true>(sc, e0 + kSuper, valid, nxt); else load16<false>(sc, e0 + kSuper, valid, nxt);
-      }
+      if (sI + 1 < n_super) load16v(vec, sc, e0 + kSuper, valid, nxt);
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
         if (e0 + j < valid) atomicAdd(&sm.hist[score_key(cur[j]) >> 20], 1u);
@@ -235,12 +385,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   int n_cand = 0;
   {
     float cur[kPer], nxt[kPer];
-    if (vec) load16<true>(sc, kPer * tid, valid, cur); else load16<false>(sc, kPer * tid, valid, cur);
+    load16v(vec, sc, kPer * tid, valid, cur);
     for (int sI = 0; sI < n_super; ++sI) {
       const int e0 = sI * kSuper + kPer * tid;
-      if (sI + 1 < n_super) {
-        if (vec) load16<true>(sc, e0 + kSuper, valid, nxt); else load16<false>(sc, e0 + kSuper, valid, nxt);
-      }
+      if (sI + 1 < n_super) load16v(vec, sc, e0 + kSuper, valid, nxt);
       uint32_t above_bits = 0u;
       int ncand = 0;
 #pragma unroll
@@ -273,9 +421,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   }
   __syncthreads();
 
-  // ---- resolve T among the candidates; add the chosen ones to the bitmap
-  uint32_t T, kk_eq;
-  select_in_candidates(sm, n_cand, kk, T, kk_eq);
+  // ---- resolve T among the candidates (all in bin b); add the chosen ones to the bitmap
+  uint32_t T, kk_eq, n_eq;
+  select_kth(sm, n_cand, kk, 1, b << 20, 0xFFF00000u, T, kk_eq, n_eq);
   {
     int tie_seen = 0;
     for (int i0 = 0; i0 < n_cand; i0 += kThreads) {
@@ -293,25 +441,31 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     }
   }
   __syncthreads();
+  write_bitmap(sm, nwords, k, out);
+}
 
-  // ---- compaction: each thread owns a run of consecutive bitmap words
-  {
-    const int per = (nwords + kThreads - 1) / kThreads;
-    const int w_begin = min(nwords, tid * per), w_end = min(nwords, w_begin + per);
-    int cnt = 0;
-    for (int w = w_begin; w < w_end; ++w) cnt += __popc(sm.bits[w]);
-    int tot;
-    int slot = block_excl_scan(cnt, sm.wsum, tot);
-    for (int w = w_begin; w < w_end; ++w) {
-      uint32_t x = sm.bits[w];
-      while (x != 0u) {
-        const int bit = __ffs(x) - 1;
-        x &= x - 1u;
-        if (slot < k) out[slot] = 32 * w + bit;
-        ++slot;
-      }
-    }
+__global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
+  __shared__ TopkSmem sm;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const int valid = max(0, min(a.valid_len[row], a.max_valid));
+  const int k = a.k;
+  int32_t* out = a.out + (size_t)row * k;
+  const float* sc = a.scores + (size_t)row * a.row_stride;
+  if (valid <= k) {
+    for (int j = tid; j < k; j += kThreads) out[j] = j < valid ? j : -1;
+    return;
   }
+  if (valid > kMaxBits) {
+    topk_radix_row(sm, sc, valid, k, out);
+    return;
+  }
+  const bool vec = ((reinterpret_cast<uintptr_t>(sc) & 15u) == 0);
+  if (valid >= kOneReadMin && k <= kCand / 4) {
+    if (topk_one_read(sm, sc, valid, k, out, vec)) return;
+    __syncthreads();
+  }
+  topk_two_reads(sm, sc, valid, k, out, vec);
 }
 
 }  // namespace

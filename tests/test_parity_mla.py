@@ -120,6 +120,56 @@ def test_topk_hook_long_and_clustered_rows(pa_lib):
         assert np.array_equal(got[r], oracle.topk_indices(scores[r].astype(np.float64), valid[r], 2048)), r
 
 
+def _sample_runs(valid):
+    """Where the top-k kernel's one-read path samples a row: 16 runs of 256 scores, run w
+    starting at w * (valid - 256) // 15 rounded down to a multiple of 4."""
+    return [((w * (valid - 256)) // 15) & ~3 for w in range(16)]
+
+
+def test_topk_hook_one_read_and_its_fallbacks(pa_lib):
+    """Rows long enough for the one-read path: plain rows, rows whose sampled runs mislead
+    the threshold both ways (too few keys reach it, too many), ties at the k-th key with
+    more copies than are taken (also +0.0 against -0.0), rows at the length limit of the
+    path and beside it, k above the path's limit, and rows that are not 16-byte aligned."""
+    import torch
+    rng = np.random.default_rng(7)
+    n = 150_000
+    rows = []
+    rows.append(rng.standard_normal(n))                                   # plain
+    r = rng.standard_normal(n)                                            # runs high: too few
+    for a in _sample_runs(n):
+        r[a:a + 256] = 10.0 + rng.standard_normal(256)
+    rows.append(r)
+    r = 10.0 + rng.standard_normal(n)                                     # runs low: too many
+    for a in _sample_runs(n):
+        r[a:a + 256] = rng.standard_normal(256)
+    rows.append(r)
+    r = rng.standard_normal(n)                                            # 2,000 ties, 1,548 taken
+    pos = rng.permutation(n)
+    r[pos[:500]] = 100.0 + np.arange(500)
+    r[pos[500:2500]] = 50.0
+    rows.append(r)
+    r = rng.standard_normal(n) - 5.0                                      # +-0 ties
+    z = rng.permutation(40_000)[:3000]
+    r[z] = np.where(rng.random(3000) < 0.5, -0.0, 0.0)
+    rows.append(r)
+    rows.append(np.round(rng.standard_normal(n) * 4) / 4)                 # few levels: bins crowd
+    scores = np.stack(rows).astype(np.float32)
+    valid = np.array([n, n, n, n, 40_000, n], np.int32)
+    for k in (2048, 1, 100, 2049):
+        got = pa_lib.pa_test_topk_from_scores(torch.from_numpy(scores).cuda(), torch.from_numpy(valid).cuda(),
+                                              k).cpu().numpy()
+        for i in range(len(rows)):
+            assert np.array_equal(got[i], oracle.topk_indices(scores[i].astype(np.float64), valid[i], k)), (k, i)
+    # lengths at the path's limit (32,768) and one below it; an odd row stride leaves rows
+    # unaligned, so the loads are scalar
+    sc = rng.standard_normal((4, 40_001)).astype(np.float32)
+    vl = np.array([32_768, 32_767, 40_001, 32_769], np.int32)
+    got = pa_lib.pa_test_topk_from_scores(torch.from_numpy(sc).cuda(), torch.from_numpy(vl).cuda(), 2048).cpu().numpy()
+    for i in range(4):
+        assert np.array_equal(got[i], oracle.topk_indices(sc[i].astype(np.float64), vl[i], 2048)), ("odd", i)
+
+
 def _indexer(pa, dev, k):
     import torch
     n_q = dev.q_idx.shape[0]
