@@ -50,12 +50,16 @@
  *   - No C++ exception crosses this interface.  Thread-safe across streams.
  *   - lse outputs (nullable) are natural-log log-sum-exp of the scaled logits, fp32.
  *   - Value domains.  Inputs must be finite.  Some operands are converted once from bf16
- *     to fp16 inside the kernels (round toward zero): the prefill's V values and the MLA
- *     / sparse-MLA queries.  The conversion is exact for magnitudes in [2^-14, 65504];
- *     smaller ones become fp16 subnormals (absolute error < 2^-25) and larger ones
- *     saturate to +-65504, so those operands must stay within +-65504.  Softmax
- *     probabilities are fed to P.V as fp16 (prefill, MLA) or as a bf16 hi + lo pair
- *     (GQA decode); FP8 values convert to fp16 / bf16 exactly.
+ *     to fp16 inside the kernels (round toward zero): the prefill's V values, and the MLA
+ *     / sparse-MLA queries in the exact recomputation kernel (units whose scores outgrow
+ *     the fixed softmax reference).  The conversion is exact for magnitudes in
+ *     [2^-14, 65504]; smaller ones become fp16 subnormals (absolute error < 2^-25) and
+ *     larger ones saturate to +-65504, so those operands must stay within +-65504.  In the
+ *     main MLA kernel each query row is scaled by a power of two (largest magnitude into
+ *     [128, 256)) and split into two E4M3 terms for the FP8 Q.K product: exact for
+ *     elements at least 2^-9 of the row's largest, absolute error <= 2^-10 in the scaled
+ *     units below that.  Softmax probabilities are fed to P.V as fp16 (prefill, MLA) or
+ *     as a bf16 hi + lo pair (GQA decode); FP8 values convert to fp16 / bf16 exactly.
  *   - Library state.  Besides the thread-local error text, the library keeps (a) the
  *     compute-unit count of each device it has run on (read once per device and process,
  *     used to size grids and the prefill split), and (b) the optional profiling tables of

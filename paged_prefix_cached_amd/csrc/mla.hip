@@ -56,7 +56,7 @@ constexpr int kKT = 32;                      // keys per tile
 constexpr int kColB = kKT * 16;              // one chunk column: 32 keys x 16 bytes
 constexpr int kTileB = kKT * kDqk;           // 18,432 bytes per tile
 constexpr int kTileLoads = kTileB / 1024;    // 18 wave-loads of 1 KB (two chunk columns each)
-constexpr int kQS = kDqk / 16;               // 36 Q.K k-steps
+constexpr int kQS = kDqk / 64;               // 9 Q.K k-steps of 64 dims (FP8 MFMA)
 constexpr int kMT = kDv / 32;                // 16 output tiles of 32 dims
 constexpr int kSelLds = 2048;                // sparse selections staged in LDS
 constexpr uint32_t kNoRow = 0xffffff;        // staged row (24 bits) of an unread selection
@@ -66,6 +66,14 @@ constexpr int kPre = 8;                      // LDS fragment reads in flight ahe
 // Source of the DMA for keys that are not to be read (a latent row and a scale of zeros) and
 // of the filler loads that keep every wave's DMA count equal: 1 KB of zeros.
 __device__ __attribute__((aligned(16))) uint8_t kZeroRow[1024] = {};
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// D = A B + C with A, B 32 x 64 / 64 x 32 E4M3 operands (32 bytes a lane, the same byte
+// order for both) and fp32 accumulation.  Zero scale operands select the unscaled form.
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
 
 // Eight FP8 (E4M3) bytes -> eight fp16 (exact), as an MFMA operand.
 __device__ __forceinline__ u32x4 fp8x8_to_f16x8(u32x2 b) {
@@ -190,19 +198,64 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   const int rows_total = SPARSE ? Hq : T * Hq;
   const int n_tiles = (n_keys + kKT - 1) / kKT;
 
-  // ---- this lane's query row (C column = lane % 32) and its Q fragments (fp16, B operand:
-  // k-step 2 j + e holds dims 32 j + 16 h + 8 e .. + 7, matching the K fragments)
+  // ---- this lane's query row (C column = lane % 32) and its Q fragments.  Q.K runs on the
+  // FP8 MFMA with the tile's E4M3 key bytes as they are: the bf16 query row, scaled by a
+  // power of two 2^qs that brings its largest magnitude into [128, 256), is split into two
+  // E4M3 terms, hi = RN(x) and lo = RN(x - hi).  A bf16 value has 8 significant bits and each
+  // term holds 4, so hi + lo = x exactly for |x| >= 2^-2 (the residual is a multiple of x's
+  // last bf16 place, at least the E4M3 subnormal step 2^-9); smaller elements, below 2^-9 of
+  // the row's largest, keep an absolute error of at most 2^-10.  K-step ks, lane half h
+  // covers dims 64 ks + 32 h .. + 31, in the same byte order for both operands.
   const int row = row0 + wave * 32 + l32;
   const bool row_ok = row < rows_total;
   const int row_c = row_ok ? row : rows_total - 1;
   const int pos = SPARSE ? 0x7fffffff : (L - T + row_c / Hq);
-  u32x4 qf[kQS];
+  i32x8 qhi[kQS], qlo[kQS];
+  float sl2;                                          // log2 units per scaled score unit
   {
-    const uint16_t* qp = qbase + (size_t)row_c * kDqk + 16 * h;
+    const uint16_t* qp = qbase + (size_t)row_c * kDqk + 32 * h;
+    u32x4 raw_q[kQS][4];
+    uint32_t amax = 0u;                               // largest |bf16| bits of the lane's dims
+#pragma unroll
+    for (int ks = 0; ks < kQS; ++ks)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        raw_q[ks][c] = ld16(qp + 64 * ks + 8 * c);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t v = raw_q[ks][c][w];
+          amax = max(amax, max(v & 0x7fffu, (v >> 16) & 0x7fffu));
+        }
+      }
+    const auto r = __builtin_amdgcn_permlane32_swap(amax, amax, false, false);
+    amax = max(r[0], r[1]);                           // the row's largest magnitude (both halves)
+    // its binade e (bf16 exponent field); qs = 7 - (e - 127), kept in the normal range
+    const int e = (int)(amax >> 7);
+    const int qs = amax == 0u ? 0 : min(126, max(-126, 134 - e));
+    const float up = __uint_as_float((uint32_t)(127 + qs) << 23);
+    sl2 = scale_log2 * __uint_as_float((uint32_t)(127 - qs) << 23);
 #pragma unroll
     for (int ks = 0; ks < kQS; ++ks) {
-      const u32x4 v = ld16(qp + 32 * (ks / 2) + 8 * (ks % 2));
-      qf[ks] = u32x4{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
+      uint32_t hw[8], lw[8];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int w2 = 0; w2 < 2; ++w2) {
+          // four bf16 values -> four hi bytes and four lo bytes (one word each)
+          const uint32_t v0 = raw_q[ks][c][2 * w2], v1 = raw_q[ks][c][2 * w2 + 1];
+          const float x0 = __uint_as_float(v0 << 16) * up, x1 = __uint_as_float(v0 & 0xffff0000u) * up;
+          const float x2 = __uint_as_float(v1 << 16) * up, x3 = __uint_as_float(v1 & 0xffff0000u) * up;
+          uint32_t hb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+          hb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, (int)hb, true);
+          const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hb, false);
+          const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hb, true);
+          uint32_t lb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0 - h01.x, x1 - h01.y, 0, false);
+          lb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2 - h23.x, x3 - h23.y, (int)lb, true);
+          hw[2 * c + w2] = hb;
+          lw[2 * c + w2] = lb;
+        }
+      qhi[ks] = i32x8{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3], (int)hw[4], (int)hw[5], (int)hw[6], (int)hw[7]};
+      qlo[ks] = i32x8{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3], (int)lw[4], (int)lw[5], (int)lw[6], (int)lw[7]};
     }
   }
 
@@ -311,9 +364,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   };
 
   // per-lane LDS offsets (bytes, relative to a tile)
-  // K fragments of k-steps 2 j and 2 j + 1: chunk 2 j + h of key l32, at this row offset
-  // inside the chunk column (odd columns swap keys r and r ^ 4)
-  const int k_row = 16 * (l32 ^ (4 * h));
   // V^T fragment of output tile mt, key step kk: within each 16-lane group g = lane / 16,
   // source lane s = 2 k + hh reads key 16 kk + 4 (g / 2) + k + 4 (k / 4) at bytes
   // 32 mt + 16 (g % 2) + 8 hh (chunk 2 mt + g % 2); the lane then holds dim 32 mt + lane % 32
@@ -323,26 +373,40 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   const int v_base = (vg & 1) * kColB + 16 * (v_key0 ^ (4 * (vg & 1))) + 8 * vhh;   // + 256 kk + 1024 mt
   lds_u8* const lds = (lds_u8*)&raw[0][0];
 
-  // S^T = K Q^T over the 36 k-steps of tile buffer B (fragment reads kPre k-steps ahead), with the
-  // row loads of the next tile spread over the pass
+  // S^T = K Q^T over the 9 k-steps of tile buffer B, two FP8 MFMAs each (Q's hi and lo terms),
+  // the key bytes fed as read; fragment reads kPre / 4 k-steps ahead, and the row loads of
+  // the next tile spread over the 18 MFMAs.  K-step ks of lane half h reads chunks
+  // 4 ks + 2 h (even: key l32 in place) and 4 ks + 2 h + 1 (odd: key l32 ^ 4).
   auto qk = [&](int B, const Dma& d) -> f32x16 {
-    const int tk = B * kTileB;
+    const int tk = B * kTileB + 2 * h * kColB;
+    const int k_even = 16 * l32, k_odd = kColB + 16 * (l32 ^ 4);
     f32x16 s0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s0[i] = 0.f;
-    constexpr int kPre2 = kPre / 2;
-    u32x4 kr[kPre2];
+    constexpr int kPreK = kPre / 4;                    // k-steps of reads in flight
+    u32x4 kr[kPreK][2];
 #pragma unroll
-    for (int j = 0; j < kPre2; ++j) kr[j] = lds_read_b128(lds, tk + (2 * j + h) * kColB + k_row);
+    for (int j = 0; j < kPreK; ++j) {
+      kr[j][0] = lds_read_b128(lds, tk + 4 * j * kColB + k_even);
+      kr[j][1] = lds_read_b128(lds, tk + 4 * j * kColB + k_odd);
+    }
+    constexpr int kMf = 2 * kQS;                       // MFMAs per tile
+    constexpr int kEvery = kMf / kLoadsMax;
 #pragma unroll
-    for (int i = 0; i < kQS; ++i) {
-      const u32x4 kq = kr[(i / 2) % kPre2];
-      const u32x2 kc = (i % 2) ? u32x2{kq.z, kq.w} : u32x2{kq.x, kq.y};
-      const int n = i / 2 + kPre2;
-      if ((i % 2) && n < kQS / 2) kr[(i / 2) % kPre2] = lds_read_b128(lds, tk + (2 * n + h) * kColB + k_row);
-      s0 = mfma32x32x16_f16(fp8x8_to_f16x8(kc), qf[i], s0);
-      constexpr int kEvery = kQS / kLoadsMax;
-      if (i % kEvery == kEvery / 2 && i / kEvery < kLoadsMax) load(d, i / kEvery);
+    for (int ks = 0; ks < kQS; ++ks) {
+      const u32x4 a0 = kr[ks % kPreK][0], a1 = kr[ks % kPreK][1];
+      const i32x8 ka = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      const int n = ks + kPreK;
+      if (n < kQS) {
+        kr[ks % kPreK][0] = lds_read_b128(lds, tk + 4 * n * kColB + k_even);
+        kr[ks % kPreK][1] = lds_read_b128(lds, tk + 4 * n * kColB + k_odd);
+      }
+#pragma unroll
+      for (int term = 0; term < 2; ++term) {
+        s0 = mfma32x32x64_fp8(ka, term ? qlo[ks] : qhi[ks], s0);
+        const int i = 2 * ks + term;
+        if (i % kEvery == kEvery / 2 && i / kEvery < kLoadsMax) load(d, i / kEvery);
+      }
     }
     return s0;
   };
@@ -369,8 +433,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   // and no clamp -- a row whose p would pass 2^kSlack is caught by the v_max check at the
   // end, and its work unit is recomputed exactly, so what it accumulated is never used.
   // Tiles whose keys are all visible (the common case) skip the mask.
-  // In log2 units a score is v = u * scale_log2 with u = s * scale_t, and p = 2^(v - m_run)
-  // is evaluated as exp2(fma(u, scale_log2, -m_run)).
+  // In log2 units a score is v = u * sl2 with u = s * scale_t (s in the query's scaled units,
+  // sl2 = scale_log2 * 2^-qs), and p = 2^(v - m_run) is evaluated as exp2(fma(u, sl2, -m_run)).
   auto softmax = [&](int B, int t, const f32x16& s0, u32x4 (&pb)[2]) {
     uint32_t okm = tmask[B];
     if constexpr (!SPARSE) {
@@ -401,7 +465,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
       // some row still lacks a reference: take it from this tile's row maximum (a row with
       // no visible key so far keeps -inf, and its p are 0)
       const float row_mx = halves_max(mx);
-      if (m_run == -INFINITY) m_run = row_mx * scale_log2;
+      if (m_run == -INFINITY) m_run = row_mx * sl2;
       m_sub = m_run == -INFINITY ? 0.f : m_run;
       all_set = __ballot(m_run == -INFINITY) == 0;
     }
@@ -413,7 +477,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
       for (int j = 0; j < 8; ++j) {
         // masked keys: p = exp2(-inf) = 0; invalid keys also have a zero scale and zero V
         const int i = 8 * kk + j;
-        const float p = fast_exp2(__builtin_fmaf(u[i], scale_log2, -m_sub));
+        const float p = fast_exp2(__builtin_fmaf(u[i], sl2, -m_sub));
         rs += p;
         pvv[j] = p * sc[i / 4][i % 4];
       }
@@ -451,7 +515,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   wait_vm<0>();                                       // no DMA outlives the workgroup
   {
     const float row_umax = halves_max(u_max);
-    const bool ovf = m_run != -INFINITY && __builtin_fmaf(row_umax, scale_log2, -m_run) > kSlack;
+    const bool ovf = m_run != -INFINITY && __builtin_fmaf(row_umax, sl2, -m_run) > kSlack;
     const bool w_ovf = __ballot(ovf) != 0;
     if (lane == 0) ovf_s[wave] = w_ovf ? 1 : 0;
   }
