@@ -10,14 +10,20 @@
 //
 // A workgroup of 8 waves owns 8 query rows (one per wave) and a chunk of keys.  Key
 // tiles of 64 tokens (one block each; the block id is read a tile ahead) are gathered
-// through the block table, upcast exactly from FP8 to bf16 and staged in LDS once for all
-// 8 queries (two buffers; the following tile's bytes are in registers meanwhile).  Each
-// wave keeps its query's 64 x 128 bf16 heads in registers (A operand) and computes
-// C[heads x keys] with v_mfma_f32_16x16x32_bf16: in the C layout a lane holds 4 heads of
-// one key, so the weighted ReLU head sum is 16 fused multiply-adds in registers (ReLU as
-// one v_med3_f32) plus a 2-step reduction across the 4 lane groups (row swaps).  The four
-// 16-key sub-tiles of a tile form one basic block, their score stores after it, so one
-// sub-tile's MFMAs overlap the previous one's head sums.
+// through the block table and staged in LDS once for all 8 queries (two buffers; the
+// following tile's bytes are in registers meanwhile).  Each wave keeps its query's 64 heads
+// in registers (A operand) and computes C[heads x keys] per 16-key sub-tile; in the C
+// layout a lane holds 4 heads of one key, so the weighted ReLU head sum is 16 fused
+// multiply-adds in registers (ReLU as one v_med3_f32) plus a 2-step reduction across the 4
+// lane groups (row swaps).  The four 16-key sub-tiles of a tile form one basic block, their
+// score stores after it, so one sub-tile's MFMAs overlap the previous one's head sums.
+//   FP8 keys: the tile stays E4M3 in LDS (144-byte rows) and feeds
+//     v_mfma_f32_16x16x128_f8f6f4 as read; each head's bf16 query row is scaled by 2^qs_h
+//     and split into two E4M3 terms (exact for elements at least 2^-9 of the head's
+//     largest), so a head tile takes two MFMAs (hi, lo), and 2^-qs_h is folded into w_h
+//     (ReLU commutes with a positive factor).
+//   MXFP4 keys: the tile is upcast to bf16 in LDS (272-byte rows) and the bf16 queries feed
+//     v_mfma_f32_16x16x32_bf16, four k-steps per head tile.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -32,7 +38,9 @@ constexpr int kWaves = PA_INDEXER_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKT = 64;                  // keys per LDS tile
 constexpr int kChunk = 8192;             // keys per workgroup
-constexpr int kKStride = kD + 8;         // bf16 per key row in LDS (272 B)
+constexpr int kKStride = kD + 8;         // bf16 per key row in LDS (272 B), MXFP4 keys
+constexpr int kKStride8 = kD + 16;       // bytes per key row in LDS (144 B), FP8 keys: the
+                                         // 16 rows of a sub-tile start in distinct banks
 
 __device__ __forceinline__ int find_seq(const int32_t* q_start, int num_seqs, int i) {
   int lo = 0, hi = num_seqs - 1;
@@ -49,7 +57,8 @@ __device__ __forceinline__ int find_seq(const int32_t* q_start, int num_seqs, in
 // in [2, 252].  Keys carry no per-token scale (1 in the score).
 template <int NHT, bool FP4>   // head tiles of 16 (num_heads / 16)
 __global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_s[2][kKT * kKStride];
+  constexpr int kRowB = FP4 ? 2 * kKStride : kKStride8;   // LDS bytes per key row
+  __shared__ __attribute__((aligned(16))) uint8_t k_s[2][kKT * kRowB];
   __shared__ float sc_s[2][kKT];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m16 = lane & 15, grp = lane >> 4;
@@ -76,23 +85,58 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
     const int blk_max_pos = min(cached + (i_last - qs), total - 1);
     const int c1 = min(c0 + kChunk, a.max_total_len);
     if (mine && chunk == 0) a.valid_len[i] = pos + 1;
-    // ---- Q in registers: A operand [16 heads x 32 dims] per (head tile, k-step)
-    u32x4 qa[NHT][4];
+    // ---- Q in registers, A operand.  MXFP4 keys: [16 heads x 32 dims] bf16 per (head
+    // tile, k-step).  FP8 keys: [16 heads x 128 dims] as two E4M3 terms per head tile, lane
+    // group grp holding dims 32 grp .. + 31 (the same byte order as the key operand).
+    u32x4 qa[FP4 ? NHT : 1][4];
+    i32x8 qhi[FP4 ? 1 : NHT], qlo[FP4 ? 1 : NHT];
     float wv[NHT][4];
     if (mine) {
       const uint16_t* qp = a.q_idx + (size_t)i * (NHT * 16) * kD;
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qa[ht][ks] = ld16(qp + (size_t)(16 * ht + m16) * kD + 32 * ks + 8 * grp);
-#pragma unroll
         for (int r = 0; r < 4; ++r) wv[ht][r] = a.w[(size_t)i * (NHT * 16) + 16 * ht + 4 * grp + r];
+        if constexpr (FP4) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) qa[ht][ks] = ld16(qp + (size_t)(16 * ht + m16) * kD + 32 * ks + 8 * grp);
+        } else {
+          u32x4 v[4];
+          uint32_t amax = 0u;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            v[c] = ld16(qp + (size_t)(16 * ht + m16) * kD + 32 * grp + 8 * c);
+            amax = bf16x8_absmax_bits(v[c], amax);
+          }
+          // the head's largest over its four lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48)
+          const auto r16 = __builtin_amdgcn_permlane16_swap(amax, amax, false, false);
+          amax = max(r16[0], r16[1]);
+          const auto r32 = __builtin_amdgcn_permlane32_swap(amax, amax, false, false);
+          const int qs = split_scale_exp(max(r32[0], r32[1]));
+          const float up = exp2i(qs);
+          uint32_t hw[8], lw[8];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            bf16x4_split_e4m3(v[c].x, v[c].y, up, hw[2 * c], lw[2 * c]);
+            bf16x4_split_e4m3(v[c].z, v[c].w, up, hw[2 * c + 1], lw[2 * c + 1]);
+          }
+          qhi[ht] = as_i32x8(u32x4{hw[0], hw[1], hw[2], hw[3]}, u32x4{hw[4], hw[5], hw[6], hw[7]});
+          qlo[ht] = as_i32x8(u32x4{lw[0], lw[1], lw[2], lw[3]}, u32x4{lw[4], lw[5], lw[6], lw[7]});
+          // C row 4 grp + r of this head tile is head 16 ht + 4 grp + r, whose qs lane 4 grp + r holds
+#pragma unroll
+          for (int r = 0; r < 4; ++r) wv[ht][r] *= exp2i(-__shfl(qs, 4 * grp + r));
+        }
       }
     } else {
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
+        if constexpr (FP4) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qa[ht][ks] = u32x4{0, 0, 0, 0};
+          for (int ks = 0; ks < 4; ++ks) qa[ht][ks] = u32x4{0, 0, 0, 0};
+        } else {
+          qhi[ht] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+          qlo[ht] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) wv[ht][r] = 0.f;
       }
@@ -143,9 +187,10 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
     auto store_tile = [&](int buf) {
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
-        uint32_t bf[8];
+        const int kj = key + (kThreads / 8) * j;
         if constexpr (FP4) {
           // byte b of each word: elements 2b (low nibble) and 2b + 1
+          uint32_t bf[8];
           const uint32_t wx = raw[j].x, wy = raw[j].y;
           const float sc = rsc[j];
           bf[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wx, sc, 0));
@@ -156,18 +201,12 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
           bf[5] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wy, sc, 1));
           bf[6] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wy, sc, 2));
           bf[7] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wy, sc, 3));
+          uint8_t* kp = k_s[buf] + kj * kRowB + 32 * dc;
+          st16(kp, u32x4{bf[0], bf[1], bf[2], bf[3]});
+          st16(kp + 16, u32x4{bf[4], bf[5], bf[6], bf[7]});
         } else {
-#pragma unroll
-          for (int w4 = 0; w4 < 4; ++w4) {
-            const u32x2 c = fp8x4_to_bf16x4(raw[j][w4]);
-            bf[2 * w4] = c.x;
-            bf[2 * w4 + 1] = c.y;
-          }
+          st16(k_s[buf] + kj * kRowB + 16 * dc, raw[j]);    // E4M3 bytes as loaded
         }
-        const int kj = key + (kThreads / 8) * j;
-        uint16_t* kp = k_s[buf] + kj * kKStride + 16 * dc;
-        st16(kp, u32x4{bf[0], bf[1], bf[2], bf[3]});
-        st16(kp + 8, u32x4{bf[4], bf[5], bf[6], bf[7]});
         if (dc == 0) sc_s[buf][kj] = FP4 ? 1.f : rsc[j];
       }
     };
@@ -196,18 +235,32 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
         float part[kKT / 16];
 #pragma unroll
         for (int st = 0; st < kKT / 16; ++st) {
-          u32x4 kb4[4];
-          const uint16_t* kp = k_s[buf] + (16 * st + m16) * kKStride + 8 * grp;
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) kb4[ks] = *reinterpret_cast<const u32x4*>(kp + 32 * ks);
           float acc = 0.f;
+          if constexpr (FP4) {
+            u32x4 kb4[4];
+            const uint8_t* kp = k_s[buf] + (16 * st + m16) * kRowB + 16 * grp;
 #pragma unroll
-          for (int ht = 0; ht < NHT; ++ht) {
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            for (int ks = 0; ks < 4; ++ks) kb4[ks] = *reinterpret_cast<const u32x4*>(kp + 64 * ks);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) c = mfma16x16x32(qa[ht][ks], kb4[ks], c);
+            for (int ht = 0; ht < NHT; ++ht) {
+              f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc = fmaf(wv[ht][r], __builtin_amdgcn_fmed3f(c[r], 0.f, 3.402823466e38f), acc);   // ReLU (finite scores)
+              for (int ks = 0; ks < 4; ++ks) c = mfma16x16x32(qa[ht][ks], kb4[ks], c);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc = fmaf(wv[ht][r], __builtin_amdgcn_fmed3f(c[r], 0.f, 3.402823466e38f), acc);   // ReLU (finite scores)
+            }
+          } else {
+            // key 16 st + m16, dims 32 grp .. + 31
+            const uint8_t* kp = k_s[buf] + (16 * st + m16) * kRowB + 32 * grp;
+            const i32x8 kb = as_i32x8(*reinterpret_cast<const u32x4*>(kp), *reinterpret_cast<const u32x4*>(kp + 16));
+#pragma unroll
+            for (int ht = 0; ht < NHT; ++ht) {
+              f32x4 c = {0.f, 0.f, 0.f, 0.f};
+              c = mfma16x16x128_fp8(qhi[ht], kb, c);
+              c = mfma16x16x128_fp8(qlo[ht], kb, c);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc = fmaf(wv[ht][r], __builtin_amdgcn_fmed3f(c[r], 0.f, 3.402823466e38f), acc);   // ReLU (finite scores)
+            }
           }
           // sum over the 4 lane groups (lanes l, l^16, l^32, l^48 hold the same key) with
           // row swaps: every lane adds the same two operands, so all copies agree

@@ -67,14 +67,6 @@ constexpr int kPre = 8;                      // LDS fragment reads in flight ahe
 // of the filler loads that keep every wave's DMA count equal: 1 KB of zeros.
 __device__ __attribute__((aligned(16))) uint8_t kZeroRow[1024] = {};
 
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-
-// D = A B + C with A, B 32 x 64 / 64 x 32 E4M3 operands (32 bytes a lane, the same byte
-// order for both) and fp32 accumulation.  Zero scale operands select the unscaled form.
-__device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
 // Eight FP8 (E4M3) bytes -> eight fp16 (exact), as an MFMA operand.
 __device__ __forceinline__ u32x4 fp8x8_to_f16x8(u32x2 b) {
   const u32x2 lo = fp8x4_to_f16x4(b.x), hi = fp8x4_to_f16x4(b.y);
@@ -199,13 +191,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   const int n_tiles = (n_keys + kKT - 1) / kKT;
 
   // ---- this lane's query row (C column = lane % 32) and its Q fragments.  Q.K runs on the
-  // FP8 MFMA with the tile's E4M3 key bytes as they are: the bf16 query row, scaled by a
-  // power of two 2^qs that brings its largest magnitude into [128, 256), is split into two
-  // E4M3 terms, hi = RN(x) and lo = RN(x - hi).  A bf16 value has 8 significant bits and each
-  // term holds 4, so hi + lo = x exactly for |x| >= 2^-2 (the residual is a multiple of x's
-  // last bf16 place, at least the E4M3 subnormal step 2^-9); smaller elements, below 2^-9 of
-  // the row's largest, keep an absolute error of at most 2^-10.  K-step ks, lane half h
-  // covers dims 64 ks + 32 h .. + 31, in the same byte order for both operands.
+  // FP8 MFMA with the tile's E4M3 key bytes as they are, the bf16 query row scaled by 2^qs
+  // and split into two E4M3 terms (bf16x4_split_e4m3: exact for elements at least 2^-9 of
+  // the row's largest).  K-step ks, lane half h covers dims 64 ks + 32 h .. + 31, in the
+  // same byte order for both operands.
   const int row = row0 + wave * 32 + l32;
   const bool row_ok = row < rows_total;
   const int row_c = row_ok ? row : rows_total - 1;
@@ -215,47 +204,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   {
     const uint16_t* qp = qbase + (size_t)row_c * kDqk + 32 * h;
     u32x4 raw_q[kQS][4];
-    uint32_t amax = 0u;                               // largest |bf16| bits of the lane's dims
+    uint32_t amax = 0u;
 #pragma unroll
     for (int ks = 0; ks < kQS; ++ks)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         raw_q[ks][c] = ld16(qp + 64 * ks + 8 * c);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t v = raw_q[ks][c][w];
-          amax = max(amax, max(v & 0x7fffu, (v >> 16) & 0x7fffu));
-        }
+        amax = bf16x8_absmax_bits(raw_q[ks][c], amax);
       }
     const auto r = __builtin_amdgcn_permlane32_swap(amax, amax, false, false);
-    amax = max(r[0], r[1]);                           // the row's largest magnitude (both halves)
-    // its binade e (bf16 exponent field); qs = 7 - (e - 127), kept in the normal range
-    const int e = (int)(amax >> 7);
-    const int qs = amax == 0u ? 0 : min(126, max(-126, 134 - e));
-    const float up = __uint_as_float((uint32_t)(127 + qs) << 23);
-    sl2 = scale_log2 * __uint_as_float((uint32_t)(127 - qs) << 23);
+    const int qs = split_scale_exp(max(r[0], r[1]));  // the row's largest (both halves)
+    const float up = exp2i(qs);
+    sl2 = scale_log2 * exp2i(-qs);
 #pragma unroll
     for (int ks = 0; ks < kQS; ++ks) {
       uint32_t hw[8], lw[8];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int w2 = 0; w2 < 2; ++w2) {
-          // four bf16 values -> four hi bytes and four lo bytes (one word each)
-          const uint32_t v0 = raw_q[ks][c][2 * w2], v1 = raw_q[ks][c][2 * w2 + 1];
-          const float x0 = __uint_as_float(v0 << 16) * up, x1 = __uint_as_float(v0 & 0xffff0000u) * up;
-          const float x2 = __uint_as_float(v1 << 16) * up, x3 = __uint_as_float(v1 & 0xffff0000u) * up;
-          uint32_t hb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-          hb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, (int)hb, true);
-          const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hb, false);
-          const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hb, true);
-          uint32_t lb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0 - h01.x, x1 - h01.y, 0, false);
-          lb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2 - h23.x, x3 - h23.y, (int)lb, true);
-          hw[2 * c + w2] = hb;
-          lw[2 * c + w2] = lb;
-        }
-      qhi[ks] = i32x8{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3], (int)hw[4], (int)hw[5], (int)hw[6], (int)hw[7]};
-      qlo[ks] = i32x8{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3], (int)lw[4], (int)lw[5], (int)lw[6], (int)lw[7]};
+      for (int c = 0; c < 4; ++c) {
+        bf16x4_split_e4m3(raw_q[ks][c].x, raw_q[ks][c].y, up, hw[2 * c], lw[2 * c]);
+        bf16x4_split_e4m3(raw_q[ks][c].z, raw_q[ks][c].w, up, hw[2 * c + 1], lw[2 * c + 1]);
+      }
+      qhi[ks] = as_i32x8(u32x4{hw[0], hw[1], hw[2], hw[3]}, u32x4{hw[4], hw[5], hw[6], hw[7]});
+      qlo[ks] = as_i32x8(u32x4{lw[0], lw[1], lw[2], lw[3]}, u32x4{lw[4], lw[5], lw[6], lw[7]});
     }
   }
 
@@ -394,8 +364,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     constexpr int kEvery = kMf / kLoadsMax;
 #pragma unroll
     for (int ks = 0; ks < kQS; ++ks) {
-      const u32x4 a0 = kr[ks % kPreK][0], a1 = kr[ks % kPreK][1];
-      const i32x8 ka = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      const i32x8 ka = as_i32x8(kr[ks % kPreK][0], kr[ks % kPreK][1]);
       const int n = ks + kPreK;
       if (n < kQS) {
         kr[ks % kPreK][0] = lds_read_b128(lds, tk + 4 * n * kColB + k_even);

@@ -66,6 +66,61 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t u) {
                                                                   __uint_as_float(u & 0xffff0000u)));
 }
 
+// ---- bf16 operands on the FP8 MFMA.  A row of bf16 values is scaled by 2^qs, which brings
+// its largest magnitude into [128, 256), and each scaled value x is split into two E4M3
+// terms, hi = RN(x) and lo = RN(x - hi).  x has 8 significant bits and each term 4, and the
+// residual x - hi is a multiple of x's last bf16 place, so hi + lo = x exactly when that
+// place is at least E4M3's subnormal step 2^-9, i.e. for |x| >= 2^-2 (elements at least 2^-9
+// of the row's largest); below that the absolute error is at most 2^-10 (scaled units).
+
+// qs for a row whose largest |bf16| has the bit pattern amax (sign cleared): 7 - (its
+// unbiased exponent), kept where 2^qs and 2^-qs are normal floats; 0 for an all-zero row.
+__device__ __forceinline__ int split_scale_exp(uint32_t amax) {
+  return amax == 0u ? 0 : min(126, max(-126, 134 - (int)(amax >> 7)));
+}
+
+// 2^e as a float, e in [-126, 127].
+__device__ __forceinline__ float exp2i(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
+
+// Largest |bf16| bit pattern among the 8 values of a 16-byte word group.
+__device__ __forceinline__ uint32_t bf16x8_absmax_bits(u32x4 v, uint32_t m) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) m = max(m, max(v[w] & 0x7fffu, (v[w] >> 16) & 0x7fffu));
+  return m;
+}
+
+// Four bf16 values (two words, low half first) times up = 2^qs -> their E4M3 hi terms and
+// lo terms, one word of four bytes each (byte i = value i).
+__device__ __forceinline__ void bf16x4_split_e4m3(uint32_t v0, uint32_t v1, float up, uint32_t& hb, uint32_t& lb) {
+  const float x0 = __uint_as_float(v0 << 16) * up, x1 = __uint_as_float(v0 & 0xffff0000u) * up;
+  const float x2 = __uint_as_float(v1 << 16) * up, x3 = __uint_as_float(v1 & 0xffff0000u) * up;
+  uint32_t h = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  h = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, (int)h, true);
+  const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h, false);
+  const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h, true);
+  uint32_t l = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0 - h01.x, x1 - h01.y, 0, false);
+  l = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2 - h23.x, x3 - h23.y, (int)l, true);
+  hb = h;
+  lb = l;
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Eight 16-byte-aligned words as one FP8 MFMA operand (32 bytes).
+__device__ __forceinline__ i32x8 as_i32x8(u32x4 a, u32x4 b) {
+  return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
+
+// FP8 (E4M3) MFMAs with fp32 accumulation: the two operands hold 32 bytes a lane in the same
+// byte order (the reduction index is laid out alike for A and B).  Zero scale operands
+// select the unscaled instruction.
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x128_fp8(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // Four OCP E4M3FN bytes -> four fp16, exact (every E4M3 value is an fp16 normal).  The
 // gfx950 scaled converter with scale 1 writes two fp16 per instruction.
 #ifndef PA_CVT_SCALED
