@@ -112,8 +112,9 @@ typedef int pa_status;
  *         41216  E8M0 key scales   [64][4]     one per 32 elements: 2^(code - 127)
  *     648 B per token against 712 B for the FP8 latent and FP8 index-key pools.  The MX
  *     format (OCP Microscaling MXFP4) is the reading of the page's "FP4 indexer"; key
- *     scale codes must lie in [2, 252] (every decoded element is then a normal bfloat16;
- *     paged_kv_append only writes such codes).  The same k pointer serves two views:
+ *     scale codes must lie in [2, 252] (paged_kv_append only writes such codes); the
+ *     indexer applies them inside its FP8 x FP4 MFMA, so each 32-element partial dot
+ *     product times 2^(code - 127) must stay within the float range.  The same k pointer serves two views:
  *       latent view   (block_size 64, num_kv_heads 1, head_dim_qk 576, head_dim_v 512)
  *                     for paged_attn_decode, sparse_mla_attn and the latent append;
  *       index view    (block_size 64, num_kv_heads 1, head_dim_qk 128, head_dim_v 0)

@@ -17,13 +17,15 @@
 // multiply-adds in registers (ReLU as one v_med3_f32) plus a 2-step reduction across the 4
 // lane groups (row swaps).  The four 16-key sub-tiles of a tile form one basic block, their
 // score stores after it, so one sub-tile's MFMAs overlap the previous one's head sums.
-//   FP8 keys: the tile stays E4M3 in LDS (144-byte rows) and feeds
-//     v_mfma_f32_16x16x128_f8f6f4 as read; each head's bf16 query row is scaled by 2^qs_h
-//     and split into two E4M3 terms (exact for elements at least 2^-9 of the head's
-//     largest), so a head tile takes two MFMAs (hi, lo), and 2^-qs_h is folded into w_h
-//     (ReLU commutes with a positive factor).
-//   MXFP4 keys: the tile is upcast to bf16 in LDS (272-byte rows) and the bf16 queries feed
-//     v_mfma_f32_16x16x32_bf16, four k-steps per head tile.
+// Each head's bf16 query row is scaled by 2^qs_h and split into two E4M3 terms (exact for
+// elements at least 2^-9 of the head's largest), so a head tile takes two FP8 MFMAs (hi,
+// lo) per 16 keys, and 2^-qs_h is folded into w_h (ReLU commutes with a positive factor).
+// The key tile stays in its stored format in LDS and is fed to the MFMA as read:
+//   FP8 keys: E4M3 rows (144 bytes apart), v_mfma_f32_16x16x128_f8f6f4;
+//   MXFP4 keys: E2M1 rows (80 bytes apart) and each row's four E8M0 codes,
+//     v_mfma_scale_f32_16x16x128_f8f6f4 with the key operand in FP4 and, per lane, the
+//     code of the 32-element group the lane holds as its scale (the MX block of the
+//     instruction is the lane's 32 elements, which is one group of the key).
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -38,9 +40,9 @@ constexpr int kWaves = PA_INDEXER_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKT = 64;                  // keys per LDS tile
 constexpr int kChunk = 8192;             // keys per workgroup
-constexpr int kKStride = kD + 8;         // bf16 per key row in LDS (272 B), MXFP4 keys
-constexpr int kKStride8 = kD + 16;       // bytes per key row in LDS (144 B), FP8 keys: the
-                                         // 16 rows of a sub-tile start in distinct banks
+// LDS bytes per key row: the 16 rows of a sub-tile start in distinct banks
+constexpr int kRowFp8 = kD + 16;         // FP8 keys: 128 bytes + 16
+constexpr int kRowFp4 = kD / 2 + 16;     // MXFP4 keys: 64 bytes + 16
 
 __device__ __forceinline__ int find_seq(const int32_t* q_start, int num_seqs, int i) {
   int lo = 0, hi = num_seqs - 1;
@@ -52,13 +54,13 @@ __device__ __forceinline__ int find_seq(const int32_t* q_start, int num_seqs, in
 }
 
 // FP4 (MXFP4 keys of the packed layout): a key row is 64 bytes, element 2j in the low
-// nibble of byte j, with one E8M0 scale code per 32 elements; the upcast to bf16 applies
-// the group scale (2^(e-127), built as the float with exponent field e), exact for codes
-// in [2, 252].  Keys carry no per-token scale (1 in the score).
+// nibble of byte j, with one E8M0 scale code per 32 elements, applied by the MFMA; keys
+// carry no per-token scale (1 in the score).
 template <int NHT, bool FP4>   // head tiles of 16 (num_heads / 16)
 __global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
-  constexpr int kRowB = FP4 ? 2 * kKStride : kKStride8;   // LDS bytes per key row
+  constexpr int kRowB = FP4 ? kRowFp4 : kRowFp8;
   __shared__ __attribute__((aligned(16))) uint8_t k_s[2][kKT * kRowB];
+  __shared__ uint8_t e_s[2][FP4 ? kKT * 4 : 4];                 // MXFP4: key r's codes at 4 r
   __shared__ float sc_s[2][kKT];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m16 = lane & 15, grp = lane >> 4;
@@ -85,58 +87,51 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
     const int blk_max_pos = min(cached + (i_last - qs), total - 1);
     const int c1 = min(c0 + kChunk, a.max_total_len);
     if (mine && chunk == 0) a.valid_len[i] = pos + 1;
-    // ---- Q in registers, A operand.  MXFP4 keys: [16 heads x 32 dims] bf16 per (head
-    // tile, k-step).  FP8 keys: [16 heads x 128 dims] as two E4M3 terms per head tile, lane
-    // group grp holding dims 32 grp .. + 31 (the same byte order as the key operand).
-    u32x4 qa[FP4 ? NHT : 1][4];
-    i32x8 qhi[FP4 ? 1 : NHT], qlo[FP4 ? 1 : NHT];
+    // ---- Q in registers, A operand: [16 heads x 128 dims] as two E4M3 terms per head
+    // tile.  The reduction index of an E4M3 operand's lane group grp is 16 grp + j for bytes
+    // j < 16 and 64 + 16 grp + j - 16 for the rest, in both operands; an E2M1 operand's lane
+    // group holds 32 grp .. + 31 in nibble order (measured).  FP8 keys: both operands take
+    // dims 32 grp .. + 31 in byte order (the same layout, so the pairing is the identity).
+    // MXFP4 keys: the key lane holds dims 32 grp .. + 31, so the query lane holds dims
+    // 16 grp .. + 15 in bytes 0-15 and 64 + 16 grp .. + 15 in bytes 16-31.
+    i32x8 qhi[NHT], qlo[NHT];
     float wv[NHT][4];
     if (mine) {
       const uint16_t* qp = a.q_idx + (size_t)i * (NHT * 16) * kD;
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
+        u32x4 v[4];
+        uint32_t amax = 0u;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) wv[ht][r] = a.w[(size_t)i * (NHT * 16) + 16 * ht + 4 * grp + r];
-        if constexpr (FP4) {
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) qa[ht][ks] = ld16(qp + (size_t)(16 * ht + m16) * kD + 32 * ks + 8 * grp);
-        } else {
-          u32x4 v[4];
-          uint32_t amax = 0u;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            v[c] = ld16(qp + (size_t)(16 * ht + m16) * kD + 32 * grp + 8 * c);
-            amax = bf16x8_absmax_bits(v[c], amax);
-          }
-          // the head's largest over its four lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48)
-          const auto r16 = __builtin_amdgcn_permlane16_swap(amax, amax, false, false);
-          amax = max(r16[0], r16[1]);
-          const auto r32 = __builtin_amdgcn_permlane32_swap(amax, amax, false, false);
-          const int qs = split_scale_exp(max(r32[0], r32[1]));
-          const float up = exp2i(qs);
-          uint32_t hw[8], lw[8];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            bf16x4_split_e4m3(v[c].x, v[c].y, up, hw[2 * c], lw[2 * c]);
-            bf16x4_split_e4m3(v[c].z, v[c].w, up, hw[2 * c + 1], lw[2 * c + 1]);
-          }
-          qhi[ht] = as_i32x8(u32x4{hw[0], hw[1], hw[2], hw[3]}, u32x4{hw[4], hw[5], hw[6], hw[7]});
-          qlo[ht] = as_i32x8(u32x4{lw[0], lw[1], lw[2], lw[3]}, u32x4{lw[4], lw[5], lw[6], lw[7]});
-          // C row 4 grp + r of this head tile is head 16 ht + 4 grp + r, whose qs lane 4 grp + r holds
-#pragma unroll
-          for (int r = 0; r < 4; ++r) wv[ht][r] *= exp2i(-__shfl(qs, 4 * grp + r));
+        for (int c = 0; c < 4; ++c) {
+          const int d0 = FP4 ? (c < 2 ? 16 * grp + 8 * c : 64 + 16 * grp + 8 * (c - 2)) : 32 * grp + 8 * c;
+          v[c] = ld16(qp + (size_t)(16 * ht + m16) * kD + d0);
+          amax = bf16x8_absmax_bits(v[c], amax);
         }
+        // the head's largest over its four lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48)
+        const auto r16 = __builtin_amdgcn_permlane16_swap(amax, amax, false, false);
+        amax = max(r16[0], r16[1]);
+        const auto r32 = __builtin_amdgcn_permlane32_swap(amax, amax, false, false);
+        const int qs = split_scale_exp(max(r32[0], r32[1]));
+        const float up = exp2i(qs);
+        uint32_t hw[8], lw[8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          bf16x4_split_e4m3(v[c].x, v[c].y, up, hw[2 * c], lw[2 * c]);
+          bf16x4_split_e4m3(v[c].z, v[c].w, up, hw[2 * c + 1], lw[2 * c + 1]);
+        }
+        qhi[ht] = as_i32x8(u32x4{hw[0], hw[1], hw[2], hw[3]}, u32x4{hw[4], hw[5], hw[6], hw[7]});
+        qlo[ht] = as_i32x8(u32x4{lw[0], lw[1], lw[2], lw[3]}, u32x4{lw[4], lw[5], lw[6], lw[7]});
+        // C row 4 grp + r of this head tile is head 16 ht + 4 grp + r, whose qs lane 4 grp + r holds
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          wv[ht][r] = a.w[(size_t)i * (NHT * 16) + 16 * ht + 4 * grp + r] * exp2i(-__shfl(qs, 4 * grp + r));
       }
     } else {
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
-        if constexpr (FP4) {
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) qa[ht][ks] = u32x4{0, 0, 0, 0};
-        } else {
-          qhi[ht] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-          qlo[ht] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-        }
+        qhi[ht] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        qlo[ht] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int r = 0; r < 4; ++r) wv[ht][r] = 0.f;
       }
@@ -152,7 +147,8 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
     static_assert(CPT * kThreads == kKT * (kD / 16), "whole chunks per thread");
     const int key = tid >> 3, dc = tid & 7;   // dims 16 dc .. 16 dc + 15 of key `key`
     u32x4 raw[CPT];                           // FP8: 16 codes; FP4: 16 codes in .x, .y
-    float rsc[CPT];                           // FP8: the key's scale; FP4: the group scale
+    float rsc[CPT];                           // FP8: the key's scale
+    uint32_t rcode[CPT];                      // FP4: the E8M0 code of the thread's group
     // A 64-key tile is exactly one 64-token block.  Its table entry is read one tile ahead
     // of its key loads (a vector load from an opaque copy of the index, so it is counted
     // with the key loads, in order, and never waits alone): the key loads of a tile never
@@ -175,8 +171,7 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
           const u32x2 c = ok ? *reinterpret_cast<const u32x2*>(a.keys + blk * a.blk_bytes + (t % kBs) * (kD / 2) + 8 * dc)
                              : u32x2{0, 0};
           raw[j] = u32x4{c.x, c.y, 0, 0};
-          const uint32_t e = ok ? a.key_sbase[blk * a.sblk_bytes + (t % kBs) * 4 + (dc >> 1)] : 127u;
-          rsc[j] = __uint_as_float(e << 23);
+          rcode[j] = ok ? a.key_sbase[blk * a.sblk_bytes + (t % kBs) * 4 + (dc >> 1)] : 127u;
         } else {
           raw[j] = ok ? ld16(a.keys + blk * a.blk_bytes + (t % kBs) * kD + 16 * dc) : u32x4{0, 0, 0, 0};
           if (dc == 0)
@@ -189,21 +184,8 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
       for (int j = 0; j < CPT; ++j) {
         const int kj = key + (kThreads / 8) * j;
         if constexpr (FP4) {
-          // byte b of each word: elements 2b (low nibble) and 2b + 1
-          uint32_t bf[8];
-          const uint32_t wx = raw[j].x, wy = raw[j].y;
-          const float sc = rsc[j];
-          bf[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wx, sc, 0));
-          bf[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wx, sc, 1));
-          bf[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wx, sc, 2));
-          bf[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wx, sc, 3));
-          bf[4] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wy, sc, 0));
-          bf[5] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wy, sc, 1));
-          bf[6] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wy, sc, 2));
-          bf[7] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wy, sc, 3));
-          uint8_t* kp = k_s[buf] + kj * kRowB + 32 * dc;
-          st16(kp, u32x4{bf[0], bf[1], bf[2], bf[3]});
-          st16(kp + 16, u32x4{bf[4], bf[5], bf[6], bf[7]});
+          *reinterpret_cast<u32x2*>(k_s[buf] + kj * kRowB + 8 * dc) = u32x2{raw[j].x, raw[j].y};
+          if ((dc & 1) == 0) e_s[buf][4 * kj + (dc >> 1)] = (uint8_t)rcode[j];
         } else {
           st16(k_s[buf] + kj * kRowB + 16 * dc, raw[j]);    // E4M3 bytes as loaded
         }
@@ -237,15 +219,16 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
         for (int st = 0; st < kKT / 16; ++st) {
           float acc = 0.f;
           if constexpr (FP4) {
-            u32x4 kb4[4];
-            const uint8_t* kp = k_s[buf] + (16 * st + m16) * kRowB + 16 * grp;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) kb4[ks] = *reinterpret_cast<const u32x4*>(kp + 64 * ks);
+            // key 16 st + m16, elements 32 grp .. + 31 (16 bytes) and their group's code
+            const int kr = 16 * st + m16;
+            const u32x4 k4 = *reinterpret_cast<const u32x4*>(k_s[buf] + kr * kRowB + 16 * grp);
+            const int code = e_s[buf][4 * kr + grp];
+            const i32x8 kb = as_i32x8(k4, u32x4{0, 0, 0, 0});
 #pragma unroll
             for (int ht = 0; ht < NHT; ++ht) {
               f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int ks = 0; ks < 4; ++ks) c = mfma16x16x32(qa[ht][ks], kb4[ks], c);
+              c = mfma16x16x128_fp8_fp4(qhi[ht], kb, code, c);
+              c = mfma16x16x128_fp8_fp4(qlo[ht], kb, code, c);
 #pragma unroll
               for (int r = 0; r < 4; ++r) acc = fmaf(wv[ht][r], __builtin_amdgcn_fmed3f(c[r], 0.f, 3.402823466e38f), acc);   // ReLU (finite scores)
             }

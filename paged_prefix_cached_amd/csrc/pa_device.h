@@ -112,13 +112,22 @@ __device__ __forceinline__ i32x8 as_i32x8(u32x4 a, u32x4 b) {
 }
 
 // FP8 (E4M3) MFMAs with fp32 accumulation: the two operands hold 32 bytes a lane in the same
-// byte order (the reduction index is laid out alike for A and B).  Zero scale operands
-// select the unscaled instruction.
+// byte order (the reduction index is laid out alike for A and B, measured), so any order
+// used for both pairs the right elements.  Zero scale operands select the unscaled
+// instruction.
 __device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mfma16x16x128_fp8(i32x8 a, i32x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+// A in E4M3 (32 bytes a lane, unscaled: code 127), B in E2M1 (16 bytes a lane in the first
+// four words, element j in nibble j) with the lane's E8M0 code b_code scaling its 32
+// elements.  The two operands' lane layouts differ (measured): B's lane group g holds
+// reduction indices 32 g .. + 31, A's holds 16 g .. + 15 (bytes 0-15) and 64 + 16 g .. + 15
+// (bytes 16-31).
+__device__ __forceinline__ f32x4 mfma16x16x128_fp8_fp4(i32x8 a, i32x8 b, int b_code, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, 127, 0, b_code);
 }
 
 // Four OCP E4M3FN bytes -> four fp16, exact (every E4M3 value is an fp16 normal).  The
