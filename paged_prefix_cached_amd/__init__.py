@@ -83,6 +83,9 @@ def load(path: str | None = None):
     p = path or LIB_PATH
     if not os.path.exists(p):
         raise PAError(f"{p} not found: build it with `python -m paged_prefix_cached_amd.build`")
+    # torch ships its own HIP runtime; importing it first makes libpa.so bind to that one.
+    # Loaded the other way round, the process would hold two HIP runtimes.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(p)
     for name, (res, args) in _SIGS.items():
         f = getattr(lib, name)
