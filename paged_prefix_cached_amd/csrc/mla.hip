@@ -9,7 +9,7 @@
 // top-k use the same sparse MQA kernel).
 //
 // MQA with d_qk = 576 (512 latent + 64 rope) and d_v = 512 (the latent itself).  Each wave
-// owns 32 query rows outright: their Q (all 576 dims, fp16) in registers and their output
+// owns 32 query rows outright: their Q (all 576 dims, two E4M3 terms) in registers and their output
 // accumulator (32 rows x 512 dims fp32) in the 256 accumulation registers, one wave per
 // SIMD.  No partial score is ever exchanged between waves; the NW waves of a workgroup
 // (NW x 32 rows) share each 32-key tile.
@@ -22,18 +22,18 @@
 // key for every chunk pair it loads (one row address per lane and tile), the Q.K fragment
 // reads of a k-step cover 512 contiguous bytes, and the transposed V reads of a half-wave
 // hit 64 distinct banks.  Per tile a wave computes
-//   S^T = K Q^T with v_mfma_f32_32x32x16_f16: lane (key r = lane % 32, half h = lane / 32)
-//     reads all 16 bytes of chunk 2 j + h of its key with one ds_read_b128 and feeds the
-//     two halves to k-steps 2 j and 2 j + 1, converted exactly to fp16 in registers (the
-//     gfx950 scaled converter, scale 1); so k-step 2 j + e covers dims 32 j + 16 h + 8 e ..
-//     + 7 of each half-wave, and the Q fragments are loaded in that order;
+//   S^T = K Q^T with v_mfma_f32_32x32x64_f8f6f4 on the key bytes as they are: lane (key
+//     r = lane % 32, half h = lane / 32) reads chunks 4 ks + 2 h and 4 ks + 2 h + 1 of its
+//     key (dims 64 ks + 32 h .. + 31) with two ds_read_b128 per k-step, and the query row,
+//     scaled by a power of two and split into two E4M3 terms, goes in as two MFMAs per
+//     k-step, its fragments in the same byte order;
 //   the softmax per row (lane = row, 16 keys; one lane-half swap per reduction), the
 //     per-token scale folded into the scores (s * scale_t) and into P (p * scale_t);
 //   O^T += V^T P^T: the V^T fragment (dim = lane % 32, 8 keys) is one ds_read_b64_tr_b8 --
 //     within each group of 16 lanes, lane i receives byte i % 8 of the 8-byte reads of lanes
 //     2k + i / 8 (k = 0..7) -- converted to fp16; the keys it covers are relabelled to match
 //     the P fragment the lane already holds.
-// LDS reads run kPre fragments ahead of their use.  Keys that are not to be read
+// LDS reads run ahead of their use (Q.K: kPre / 4 k-steps; V^T: kPre fragments).  Keys that are not to be read
 // (unselected, past the range, bad block id) are fetched from a row of zeros: zero K, V and
 // scale, and their scores are masked to -inf.
 //
