@@ -565,6 +565,9 @@ def bench_append(steps, warmup):
     is5 = torch.empty((a5.num_blocks, 64), dtype=torch.float32, device="cuda")
     mla5, idx5 = pa.mla_pool(p5, s5), pa.indexer_pool(i5, is5)
     x5, xi5 = rows(4096, 576), rows(4096, 128)
+    # the same rows into the packed per-block layout: latent view and MXFP4 index view
+    blocks5 = torch.empty((a5.num_blocks, W.PACKED_BLOCK_BYTES), dtype=torch.uint8, device="cuda")
+    lat5p, idx5p = pa.packed_mla_pools(blocks5)
     torch.cuda.synchronize()
 
     def step():
@@ -572,17 +575,21 @@ def bench_append(steps, warmup):
         pa.paged_kv_append(mla4, *d4, x4, max_new_len=4)
         pa.paged_kv_append(mla5, *d5, x5, max_new_len=4096)
         pa.paged_kv_append(idx5, *d5, xi5, max_new_len=4096)
+        pa.paged_kv_append(lat5p, *d5, x5, max_new_len=4096)
+        pa.paged_kv_append(idx5p, *d5, xi5, max_new_len=4096)
 
     tm = timed_steps(step, steps, warmup)
     ms = tm["ms"]
     gqa_bytes = 2 * (16384 * 8 * 128 * 2 * 2)
-    fp8_bytes = 256 * (576 * 3 + 4) + 4096 * (576 * 3 + 4) + 4096 * (128 * 3 + 4)
+    fp8_bytes = 256 * (576 * 3 + 4) + 2 * 4096 * (576 * 3 + 4) + 4096 * (128 * 3 + 4)
+    fp4_bytes = 4096 * (128 * 2 + 64 + 4)        # bf16 row read, 64 code bytes + 4 E8M0 codes written
     k_ms = _kmean(tm, "append_gqa")
     ach = gqa_bytes / (k_ms * 1e-3) / 1e9
     return {"workload": "KV append: 8 x 2048 bf16 rows (8 KV heads x 128) + 64 x 4 and 4096 FP8 latent "
-                        "rows (576) + 4096 FP8 indexer rows (128), per-token quantisation",
-            "ms": ms, "kernel_ms": _kms(tm), "bytes": gqa_bytes + fp8_bytes,
-            "gbps": (gqa_bytes + fp8_bytes) / (ms * 1e-3) / 1e9,
+                        "rows (576) + 4096 FP8 indexer rows (128), per-token quantisation; the 4096 latent "
+                        "and indexer rows again into the packed layout (FP8 latent, MXFP4 index keys)",
+            "ms": ms, "kernel_ms": _kms(tm), "bytes": gqa_bytes + fp8_bytes + fp4_bytes,
+            "gbps": (gqa_bytes + fp8_bytes + fp4_bytes) / (ms * 1e-3) / 1e9,
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": ach / HBM_PEAK_GBS, "kernel": "append_gqa_kernel"}}
 

@@ -661,8 +661,8 @@ pa_status paged_kv_append(const pa_kv_pool* pool, const int32_t* block_table, in
   a.num_kv_heads = pool->num_kv_heads;
   a.head_dim = pool->head_dim_qk;
   a.is_fp8 = fp8 ? 1 : 0;
-  return launched(timed(fp8 ? "append_fp8" : "append_gqa", stream, [&] { return pa::launch_append(a, stream); }),
-                  "append launch");
+  const char* tname = !fp8 ? "append_gqa" : (a.mxfp4 ? "append_mxfp4" : "append_fp8");
+  return launched(timed(tname, stream, [&] { return pa::launch_append(a, stream); }), "append launch");
 }
 
 // ------------------------------------------------------------------------- test hooks
