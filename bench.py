@@ -46,6 +46,12 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 FP8_PEAK_TFLOPS = 5000.0
 DECODE_SOURCES = ["paged_prefix_cached_amd/csrc/decode_gqa.hip", "paged_prefix_cached_amd/csrc/pa_device.h",
                   "paged_prefix_cached_amd/csrc/pa_internal.h"]
+_HDRS = ["paged_prefix_cached_amd/csrc/pa_device.h", "paged_prefix_cached_amd/csrc/pa_internal.h"]
+PREFILL_SOURCES = ["paged_prefix_cached_amd/csrc/prefill_gqa.hip"] + _HDRS
+MLA_SOURCES = ["paged_prefix_cached_amd/csrc/mla.hip"] + _HDRS
+INDEXER_SOURCES = ["paged_prefix_cached_amd/csrc/indexer.hip"] + _HDRS
+TOPK_SOURCES = ["paged_prefix_cached_amd/csrc/topk.hip"] + _HDRS
+SPARSE_PROFILE = "indexer_topk_sparse_mla.131072+4096.txt"
 
 
 def log(*a):
@@ -180,26 +186,32 @@ def _mfma_roof(flops, k_ms, kernel, per_unit, peak=None, dtype="fp16", peak_note
     return r
 
 
-def measured_traffic(counters_file: str, sources: list[str]):
+def measured_traffic(counters_file: str, sources: list[str], section: str | None = None):
     """HBM bytes per launch from a committed rocprofv3 counter summary (FETCH_SIZE and
     WRITE_SIZE, scaled by a copy-kernel calibration), or None when the summary is absent
-    or was taken on different kernel sources (sha256 over `sources`)."""
+    or was taken on different kernel sources (sha256 over `sources`).  `section` selects the
+    block whose "[...]" title starts with it, in summaries that cover several kernels."""
     import hashlib
     path = os.path.join(ROOT, "profiles", counters_file)
     if not os.path.exists(path):
         return None
     fields = {}
+    inside = section is None
     for line in open(path):
-        if ":" in line and not line.startswith("#"):
+        if line.startswith("["):
+            if section is not None:
+                inside = line[1:].startswith(section)
+            continue
+        if inside and ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
-            fields[k.strip()] = v.strip()
+            fields[k.strip()] = v.strip().split()[0] if v.strip() else ""
     h = hashlib.sha256()
     for src in sources:
         with open(os.path.join(ROOT, src), "rb") as f:
             h.update(f.read())
     if fields.get("source_sha256") != h.hexdigest():
         return None
-    return float(fields["traffic_bytes_per_launch"])
+    return float(fields["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in fields else None
 
 
 # --------------------------------------------------------------------------- decode (headline)
@@ -367,8 +379,11 @@ def bench_prefill(steps, warmup):
     t = time.time()
     wl = W.make_prefix_prefill(3)
     log(f"[bench] prefill workload ready in {time.time() - t:.1f}s")
-    return _bench_gqa_prefill_workload(
+    r = _bench_gqa_prefill_workload(
         wl, "prefix-cached suffix prefill: 8 seqs x (142000 cached + 2048 new), 32q/8kv, d128, bf16", steps, warmup)
+    r["roofline"]["traffic"] = measured_traffic("gqa_prefill_kernel.suffix-prefill-8x142000+2048.txt",
+                                                PREFILL_SOURCES, section="gqa_prefill_kernel")
+    return r
 
 
 def bench_cold(steps, warmup):
@@ -460,6 +475,8 @@ def bench_mla(steps, warmup):
     k_ms = _kmean(tm, "decode_mla")
     roof = _mfma_roof(flops, k_ms, "mla_kernel (decode)", "2 x (576 + 512) FLOP per (query row, visible key)",
                       peak_note=SPLIT_PEAK_NOTE)
+    roof["traffic"] = measured_traffic("mla_kernel.mla-mtp3-decode-64seq-ctx32k-256k.txt", MLA_SOURCES,
+                                       section="mla_kernel<false")
     roof["hbm_frac"] = kv_bytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
     return {"workload": "MLA latent decode MTP3: 64 seqs x 4 tokens, 64 heads, FP8 latent 512+64, "
                         "contexts U[32768, 262144], block 64",
@@ -516,6 +533,12 @@ def bench_sparse(steps, warmup, packed=False):
         "sparse_mla": _mfma_roof(sp_flops, _kmean(tm, "sparse_mla"), "mla_kernel (sparse)",
                                  "2 x (576 + 512) FLOP per (query row, selected key)", peak_note=SPLIT_PEAK_NOTE),
     }
+    # counter traffic from the committed summary, while the kernels' sources are unchanged
+    tag = "MXFP4 keys, packed layout" if packed else "FP8 keys"
+    roofs["indexer"]["traffic"] = measured_traffic(SPARSE_PROFILE, INDEXER_SOURCES, section=f"indexer_kernel<4> ({tag})")
+    roofs["topk"]["traffic"] = measured_traffic(SPARSE_PROFILE, TOPK_SOURCES, section=f"topk_kernel ({tag} run)")
+    roofs["sparse_mla"]["traffic"] = measured_traffic(SPARSE_PROFILE, MLA_SOURCES,
+                                                      section=f"mla_kernel<true, 2, 4, true> (sparse, {tag} run)")
     L = int(mla.total_len[0])
     kv_per_token = 576 + 4 + (64 + 4 if packed else 128 + 4)
     return {"workload": ("packed per-block layout: MXFP4 indexer keys" if packed else "indexer (FP8 keys)")
