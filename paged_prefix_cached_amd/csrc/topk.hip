@@ -7,50 +7,48 @@
 // is a known hotspot).
 //
 // Scores are compared through order-preserving 32-bit keys (-0.0 keyed as +0.0, so the
-// two zeros tie).  One workgroup of 1,024 threads per row.
+// two zeros tie).  One workgroup of 512 threads per row, two workgroups per CU (72 KB of
+// LDS each), so one row's selection runs while the other row is being read.
 //
-// One read (rows of at least kOneReadMin tokens, k <= kCand / 4): a sample of 4,096
-// scores from 16 evenly spaced runs of the row gives, by a two-level LDS histogram, a key
-// threshold tau that about 2k of the row's keys reach.  The row is then read once; every
-// key >= tau is appended (key, token) to an LDS candidate list, each wave reserving its
-// slots with one LDS atomic per 16,384-score step, so the pass has no barrier.  If at
-// least k and at most kCand keys reached tau, the list holds the whole top k (the k-th
-// largest key of the row is >= tau); a radix select over the list finds T, the k-th
-// largest key, and how many keys equal to T to take; the taken ties (lowest tokens first,
-// through an index-ordered scan of an LDS bitmap) and the keys above T set their bits in
-// the bitmap, and a prefix sum over its popcounts writes the tokens in ascending order.
-// Otherwise (the sample misled: too few or too many keys reached tau) the row takes the
-// two-read path below.
-//
-// Two reads (shorter rows, and the fallback):
-//   1. a 4,096-bin LDS histogram of the top 12 key bits locates the bin b holding the
-//      k-th largest key, with G keys above it;
-//   2. in index order, keys above b set their bit in the bitmap and keys in b are
-//      appended, in index order, to the candidate list;
-// then, in LDS only: a radix select over the candidates' low 20 bits finds T and the
-// number of ties to take; candidates above T and the first such ties (in index order)
-// join the bitmap, which is compacted as above.
-// Rows longer than the bitmap or whose bin b overflows the candidate list fall back to
-// four 8-bit radix passes over the row plus an index-ordered compaction pass.
+// A row is selected through a key threshold tau that at least k of its keys reach:
+//   1. tau: rows of at least kOneReadMin tokens with k <= kCand / 4 take it from a sample of
+//      4,096 scores (8 evenly spaced runs of 512) by a two-level LDS histogram (top 11 key
+//      bits, then the next 9 inside the chosen bin), aimed at about 2k keys; other rows take
+//      the bin of the k-th largest key from a full-row 2,048-bin histogram (one more read);
+//   2. one pass over the row appends every key >= tau (key, token) to an LDS candidate list,
+//      each wave reserving its slots with one LDS atomic per 8,192-score step (no barrier);
+//   3. if at least k and at most kCand keys reached tau, the list holds the whole top k (the
+//      k-th largest key is >= tau): a three-pass radix select (11 + 11 + 10 bits) over the
+//      list finds T, the k-th largest key, and how many keys equal to T to take; each
+//      candidate's class (above T, equal, below) is folded into its token entry, and the
+//      keys' LDS is then reused as a token bitmap: the taken ties (lowest tokens first,
+//      through an index-ordered popcount scan) and the keys above T set their bits, and a
+//      prefix sum over the popcounts writes the tokens in ascending order.
+// A sampled tau that leaves fewer than k or more than kCand candidates falls back to the
+// full-histogram tau; a bin holding more than kCand keys above the threshold, or a row
+// longer than the bitmap, falls back to four 8-bit radix passes over the row plus an
+// index-ordered compaction pass.
 #include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 512;               // two workgroups per CU
 constexpr int kWaves = kThreads / 64;
-constexpr int kBins = 4096;                 // top 12 key bits
+constexpr int kBins = 2048;                 // top 11 key bits
 constexpr int kMaxBits = 1 << 18;           // bitmap capacity (tokens per row)
 constexpr int kWords = kMaxBits / 32;
 constexpr int kCand = 8192;                 // candidate list capacity
-constexpr int kSampleRun = 256;             // sample: one run of 256 scores per wave (4 a lane)
+constexpr int kSampleRun = 512;             // sample: one run of 512 scores per wave (8 a lane)
 constexpr int kSample = kWaves * kSampleRun;  // 4,096 sampled scores
-constexpr int kOneReadMin = 32768;          // shortest row that tries the one-read path
+constexpr int kOneReadMin = 32768;          // shortest row that tries the sampled threshold
 constexpr int kMinRank = 64;                // smallest sample rank used for the threshold
 constexpr int kPer = 16;                    // scores per thread and step
 constexpr int kSuper = kThreads * kPer;     // scores per workgroup step
+constexpr uint32_t kTokMask = (1u << 30) - 1;  // token bits of a candidate entry
 static_assert(kBins <= 4 * kThreads, "bin search covers 4 bins a thread");
+static_assert(kWords == kCand, "the bitmap reuses the candidates' key array");
 static_assert(kOneReadMin / kWaves >= kSampleRun, "sample runs do not overlap");
 
 __device__ __forceinline__ uint32_t score_key(float f) {
@@ -58,7 +56,7 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// 16 consecutive scores from sc[e0 ..] as keys; positions at or past `valid` get flag 0.
+// 16 consecutive scores from sc[e0 ..]; positions at or past `valid` read as 0.
 // VEC: sc + e0 is 16-byte aligned (four 16-byte loads), else scalar loads.
 template <bool VEC>
 __device__ __forceinline__ void load16(const float* sc, int e0, int valid, float (&f)[16]) {
@@ -103,9 +101,11 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
 
 struct TopkSmem {
   uint32_t hist[kBins];
-  uint32_t bits[kWords];
-  int32_t cidx[kCand];
-  uint32_t ckey[kCand];
+  uint32_t cidx[kCand];                     // candidate tokens (bits 30-31: class after the select)
+  union {
+    uint32_t ckey[kCand];                   // candidate keys, until T is known
+    uint32_t bits[kWords];                  // then the token bitmap
+  };
   int wsum[kWaves];
   uint32_t sh_bin, sh_kk, sh_n;
   int n_cand;
@@ -134,58 +134,6 @@ __device__ void find_bin_from_top(TopkSmem& sm, int nbins, uint32_t kk) {
     above += (int)c[i];
   }
   __syncthreads();
-}
-
-// Radix select in LDS: the kk-th largest key among ckey[0..n) whose bits under `mask` equal
-// `prefix`, over the key fields from `first` on (bits 31..20, 19..8, 7..0).  Returns T,
-// the number of keys equal to T that are taken (kk_eq) and the number of keys equal to T
-// among the filtered ones (n_eq).
-__device__ void select_kth(TopkSmem& sm, int n, uint32_t kk, int first, uint32_t prefix, uint32_t mask,
-                           uint32_t& T, uint32_t& kk_eq, uint32_t& n_eq) {
-  const int tid = threadIdx.x;
-  const int shifts[3] = {20, 8, 0};
-  const int widths[3] = {12, 12, 8};
-  uint32_t cnt = 0;
-  for (int pass = first; pass < 3; ++pass) {
-    const int sh = shifts[pass], nb = 1 << widths[pass];
-    for (int j = tid; j < nb; j += kThreads) sm.hist[j] = 0u;
-    __syncthreads();
-    for (int i = tid; i < n; i += kThreads) {
-      const uint32_t u = sm.ckey[i];
-      if ((u & mask) == prefix) atomicAdd(&sm.hist[(u >> sh) & (nb - 1)], 1u);
-    }
-    __syncthreads();
-    find_bin_from_top(sm, nb, kk);
-    prefix |= sm.sh_bin << sh;
-    kk = sm.sh_kk;
-    cnt = sm.sh_n;
-    mask |= (uint32_t)(nb - 1) << sh;
-    __syncthreads();
-  }
-  T = prefix;
-  kk_eq = kk;
-  n_eq = cnt;
-}
-
-// The bitmap's set bits, in ascending token order, to out[0..k): each thread owns a run
-// of consecutive words.
-__device__ void write_bitmap(TopkSmem& sm, int nwords, int k, int32_t* out) {
-  const int tid = threadIdx.x;
-  const int per = (nwords + kThreads - 1) / kThreads;
-  const int w_begin = min(nwords, tid * per), w_end = min(nwords, w_begin + per);
-  int cnt = 0;
-  for (int w = w_begin; w < w_end; ++w) cnt += __popc(sm.bits[w]);
-  int tot;
-  int slot = block_excl_scan(cnt, sm.wsum, tot);
-  for (int w = w_begin; w < w_end; ++w) {
-    uint32_t x = sm.bits[w];
-    while (x != 0u) {
-      const int bit = __ffs(x) - 1;
-      x &= x - 1u;
-      if (slot < k) out[slot] = 32 * w + bit;
-      ++slot;
-    }
-  }
 }
 
 // Fallback: four 8-bit radix passes over the row, then an index-ordered compaction.
@@ -225,49 +173,84 @@ __device__ void topk_radix_row(TopkSmem& sm, const float* sc, int valid, int k, 
   }
 }
 
-// One read of the row (see the file comment).  Returns false, uniformly over the
-// workgroup and with nothing written to out, when the sampled threshold did not leave
-// between k and kCand candidates; the caller then runs the two-read path.
-// Requires kOneReadMin <= valid <= kMaxBits and k <= kCand / 4.
-__device__ bool topk_one_read(TopkSmem& sm, const float* sc, int valid, int k, int32_t* out, bool vec) {
+// tau from a sample of the row (see the file comment); the first step's loads are issued
+// by the caller before this runs.  Requires kOneReadMin <= valid.
+__device__ uint32_t sampled_tau(TopkSmem& sm, const float* sc, int valid, int k, bool vec) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_super = (valid + kSuper - 1) / kSuper;
-  // The first step's loads go out before the sample is processed.
-  float cur[kPer], nxt[kPer];
-  load16v(vec, sc, kPer * tid, valid, cur);
-
-  // ---- sample: run w (wave w) starts at w (valid - 256) / 15, rounded down to 4 scores
+  // run w (wave w) starts at w (valid - 512) / 7, rounded down to 4 scores; lane l takes
+  // scores 4 l .. + 3 and 256 + 4 l .. + 3 of it
   const int r0 = (int)(((long long)wave * (valid - kSampleRun) / (kWaves - 1)) & ~3ll);
-  uint32_t skey[4];
-  if (vec) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(sc + r0 + 4 * lane);
-    skey[0] = score_key(v.x); skey[1] = score_key(v.y); skey[2] = score_key(v.z); skey[3] = score_key(v.w);
-  } else {
+  uint32_t skey[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) skey[i] = score_key(sc[r0 + 4 * lane + i]);
+  for (int hh = 0; hh < 2; ++hh) {
+    const int e = r0 + 256 * hh + 4 * lane;
+    if (vec) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(sc + e);
+      skey[4 * hh] = score_key(v.x); skey[4 * hh + 1] = score_key(v.y);
+      skey[4 * hh + 2] = score_key(v.z); skey[4 * hh + 3] = score_key(v.w);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) skey[4 * hh + i] = score_key(sc[e + i]);
+    }
   }
   for (int j = tid; j < kBins; j += kThreads) sm.hist[j] = 0u;
-  if (tid == 0) sm.n_cand = 0;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) atomicAdd(&sm.hist[skey[i] >> 20], 1u);
+  for (int i = 0; i < 8; ++i) atomicAdd(&sm.hist[skey[i] >> 21], 1u);
   __syncthreads();
   // rank in the sample whose key about 2k of the row's keys reach (at least kMinRank, so
   // that the count stays close to its expectation)
   const int want = (int)(((long long)2 * k * kSample + valid - 1) / valid);
   const uint32_t rank = (uint32_t)min(kSample, max(kMinRank, want));
   find_bin_from_top(sm, kBins, rank);
-  const uint32_t b12 = sm.sh_bin, rr = sm.sh_kk;
-  for (int j = tid; j < 256; j += kThreads) sm.hist[j] = 0u;
+  const uint32_t b11 = sm.sh_bin, rr = sm.sh_kk;
+  for (int j = tid; j < 512; j += kThreads) sm.hist[j] = 0u;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if ((skey[i] >> 20) == b12) atomicAdd(&sm.hist[(skey[i] >> 12) & 255u], 1u);
+  for (int i = 0; i < 8; ++i)
+    if ((skey[i] >> 21) == b11) atomicAdd(&sm.hist[(skey[i] >> 12) & 511u], 1u);
   __syncthreads();
-  find_bin_from_top(sm, 256, rr);
-  const uint32_t tau = (b12 << 20) | (sm.sh_bin << 12);
+  find_bin_from_top(sm, 512, rr);
+  return (b11 << 21) | (sm.sh_bin << 12);
+}
 
-  // ---- the row, once: keys >= tau to the candidate list (slots reserved per wave)
+// tau = the lowest key of the bin holding the k-th largest key (a full-row histogram of
+// the top 11 key bits; one read of the row).  Returns false when the keys from that bin
+// up number more than kCand.  Requires k < valid.
+__device__ bool exact_tau(TopkSmem& sm, const float* sc, int valid, int k, bool vec, uint32_t& tau) {
+  const int tid = threadIdx.x;
+  const int n_super = (valid + kSuper - 1) / kSuper;
+  for (int j = tid; j < kBins; j += kThreads) sm.hist[j] = 0u;
+  __syncthreads();
+  float cur[kPer], nxt[kPer];
+  load16v(vec, sc, kPer * tid, valid, cur);
+  for (int sI = 0; sI < n_super; ++sI) {
+    const int e0 = sI * kSuper + kPer * tid;
+    if (sI + 1 < n_super) load16v(vec, sc, e0 + kSuper, valid, nxt);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (e0 + j < valid) atomicAdd(&sm.hist[score_key(cur[j]) >> 21], 1u);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) cur[j] = nxt[j];
+  }
+  __syncthreads();
+  find_bin_from_top(sm, kBins, (uint32_t)k);
+  // keys from the bin up: the (k - kk) above it plus the bin's own
+  const int above_and_bin = k - (int)sm.sh_kk + (int)sm.sh_n;
+  tau = sm.sh_bin << 21;
+  return above_and_bin <= kCand;
+}
+
+// Steps 2 and 3 of the file comment for a threshold tau.  cur holds the first step's
+// scores (loads issued by the caller).  Returns false, uniformly over the workgroup and with
+// nothing written to out, when fewer than k or more than kCand keys reached tau.
+__device__ bool select_from(TopkSmem& sm, const float* sc, int valid, int k, int32_t* out, bool vec, uint32_t tau,
+                            float (&cur)[kPer]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int n_super = (valid + kSuper - 1) / kSuper;
+  if (tid == 0) sm.n_cand = 0;
+  __syncthreads();
+  float nxt[kPer];
   for (int sI = 0; sI < n_super; ++sI) {
     const int e0 = sI * kSuper + kPer * tid;
     if (sI + 1 < n_super) load16v(vec, sc, e0 + kSuper, valid, nxt);
@@ -292,7 +275,7 @@ __device__ bool topk_one_read(TopkSmem& sm, const float* sc, int valid, int k, i
                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
           if (s_j < kCand) {
             sm.ckey[s_j] = score_key(cur[j]);
-            sm.cidx[s_j] = e0 + j;
+            sm.cidx[s_j] = (uint32_t)(e0 + j);
           }
         }
         slot += __popcll(bal);
@@ -305,16 +288,46 @@ __device__ bool topk_one_read(TopkSmem& sm, const float* sc, int valid, int k, i
   const int n = sm.n_cand;
   if (n < k || n > kCand) return false;
 
-  // ---- T, the k-th largest key among the candidates, and the ties to take
-  uint32_t T, kk_eq, n_eq;
-  select_kth(sm, n, (uint32_t)k, 0, 0u, 0u, T, kk_eq, n_eq);
+  // ---- T, the k-th largest key among the candidates (radix select, LDS histograms over
+  // bits 31..21, 20..10, 9..0), and the ties to take
+  uint32_t prefix = 0u, mask = 0u, kk = (uint32_t)k, n_eq = 0u;
+  {
+    const int shifts[3] = {21, 10, 0};
+    const int widths[3] = {11, 11, 10};
+    for (int pass = 0; pass < 3; ++pass) {
+      const int sh = shifts[pass], nb = 1 << widths[pass];
+      for (int j = tid; j < nb; j += kThreads) sm.hist[j] = 0u;
+      __syncthreads();
+      for (int i = tid; i < n; i += kThreads) {
+        const uint32_t u = sm.ckey[i];
+        if ((u & mask) == prefix) atomicAdd(&sm.hist[(u >> sh) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      find_bin_from_top(sm, nb, kk);
+      prefix |= sm.sh_bin << sh;
+      kk = sm.sh_kk;
+      n_eq = sm.sh_n;
+      mask |= (uint32_t)(nb - 1) << sh;
+      __syncthreads();
+    }
+  }
+  const uint32_t T = prefix, kk_eq = kk;
+  // each candidate's class into its token entry: 2 above T, 1 equal, 0 below
+  for (int i = tid; i < n; i += kThreads) {
+    const uint32_t u = sm.ckey[i];
+    sm.cidx[i] |= (u > T ? 2u : (u == T ? 1u : 0u)) << 30;
+  }
+  __syncthreads();
+  // the keys are no longer needed: their array becomes the bitmap
   const int nwords = (valid + 31) / 32;
   for (int j = tid; j < nwords; j += kThreads) sm.bits[j] = 0u;
   __syncthreads();
   if (n_eq != kk_eq) {
     // more keys equal T than are taken: keep the kk_eq lowest tokens among them
-    for (int i = tid; i < n; i += kThreads)
-      if (sm.ckey[i] == T) atomicOr(&sm.bits[sm.cidx[i] >> 5], 1u << (sm.cidx[i] & 31));
+    for (int i = tid; i < n; i += kThreads) {
+      const uint32_t e = sm.cidx[i];
+      if ((e >> 30) == 1u) atomicOr(&sm.bits[(e & kTokMask) >> 5], 1u << (e & 31));
+    }
     __syncthreads();
     const int per = (nwords + kThreads - 1) / kThreads;
     const int w_begin = min(nwords, tid * per), w_end = min(nwords, w_begin + per);
@@ -333,118 +346,40 @@ __device__ bool topk_one_read(TopkSmem& sm, const float* sc, int valid, int k, i
       sm.bits[w] = keep;
     }
     __syncthreads();
-    for (int i = tid; i < n; i += kThreads)
-      if (sm.ckey[i] > T) atomicOr(&sm.bits[sm.cidx[i] >> 5], 1u << (sm.cidx[i] & 31));
+    for (int i = tid; i < n; i += kThreads) {
+      const uint32_t e = sm.cidx[i];
+      if ((e >> 30) == 2u) atomicOr(&sm.bits[(e & kTokMask) >> 5], 1u << (e & 31));
+    }
   } else {
-    for (int i = tid; i < n; i += kThreads)
-      if (sm.ckey[i] >= T) atomicOr(&sm.bits[sm.cidx[i] >> 5], 1u << (sm.cidx[i] & 31));
+    for (int i = tid; i < n; i += kThreads) {
+      const uint32_t e = sm.cidx[i];
+      if ((e >> 30) != 0u) atomicOr(&sm.bits[(e & kTokMask) >> 5], 1u << (e & 31));
+    }
   }
   __syncthreads();
-  write_bitmap(sm, nwords, k, out);
+  // ---- the bitmap's set bits, in ascending token order, to out[0..k): each thread owns a
+  // run of consecutive words
+  {
+    const int per = (nwords + kThreads - 1) / kThreads;
+    const int w_begin = min(nwords, tid * per), w_end = min(nwords, w_begin + per);
+    int cnt = 0;
+    for (int w = w_begin; w < w_end; ++w) cnt += __popc(sm.bits[w]);
+    int tot;
+    int slot = block_excl_scan(cnt, sm.wsum, tot);
+    for (int w = w_begin; w < w_end; ++w) {
+      uint32_t x = sm.bits[w];
+      while (x != 0u) {
+        const int bit = __ffs(x) - 1;
+        x &= x - 1u;
+        if (slot < k) out[slot] = 32 * w + bit;
+        ++slot;
+      }
+    }
+  }
   return true;
 }
 
-// Two reads of the row (see the file comment).  Requires k < valid <= kMaxBits.
-__device__ void topk_two_reads(TopkSmem& sm, const float* sc, int valid, int k, int32_t* out, bool vec) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  // Both passes walk the row in steps of 16 consecutive scores per thread (16,384 per
-  // workgroup step), the next step's loads in flight while the current one is processed.
-  const int n_super = (valid + kSuper - 1) / kSuper;
-
-  // ---- pass 1: histogram of the top 12 key bits
-  for (int j = tid; j < kBins; j += kThreads) sm.hist[j] = 0u;
-  __syncthreads();
-  {
-    float cur[kPer], nxt[kPer];
-    load16v(vec, sc, kPer * tid, valid, cur);
-    for (int sI = 0; sI < n_super; ++sI) {
-      const int e0 = sI * kSuper + kPer * tid;
-      if (sI + 1 < n_super) load16v(vec, sc, e0 + kSuper, valid, nxt);
-#pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        if (e0 + j < valid) atomicAdd(&sm.hist[score_key(cur[j]) >> 20], 1u);
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) cur[j] = nxt[j];
-    }
-  }
-  __syncthreads();
-  // bin b with G keys above it and G < k <= G + hist[b]
-  find_bin_from_top(sm, kBins, (uint32_t)k);
-  const uint32_t b = sm.sh_bin, kk = sm.sh_kk;
-  const int nb = (int)sm.sh_n;
-  if (nb > kCand) {
-    __syncthreads();
-    topk_radix_row(sm, sc, valid, k, out);
-    return;
-  }
-
-  // ---- pass 2: bitmap of keys above b, index-ordered candidate list of keys in b
-  const int nwords = (valid + 31) / 32;
-  for (int j = tid; j < nwords; j += kThreads) sm.bits[j] = 0u;
-  __syncthreads();
-  int n_cand = 0;
-  {
-    float cur[kPer], nxt[kPer];
-    load16v(vec, sc, kPer * tid, valid, cur);
-    for (int sI = 0; sI < n_super; ++sI) {
-      const int e0 = sI * kSuper + kPer * tid;
-      if (sI + 1 < n_super) load16v(vec, sc, e0 + kSuper, valid, nxt);
-      uint32_t above_bits = 0u;
-      int ncand = 0;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const uint32_t hb = score_key(cur[j]) >> 20;
-        const bool in = e0 + j < valid;
-        above_bits |= (in && hb > b) ? (1u << j) : 0u;
-        ncand += (in && hb == b) ? 1 : 0;
-      }
-      // two threads' 16 bits form one bitmap word (elements e0 .. e0 + 31)
-      const uint32_t other = __shfl_xor(above_bits, 1);
-      if ((lane & 1) == 0 && (e0 >> 5) < nwords) sm.bits[e0 >> 5] = above_bits | (other << 16);
-      int tot;
-      int pos = n_cand + block_excl_scan(ncand, sm.wsum, tot);
-      if (ncand) {
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-          const uint32_t u = score_key(cur[j]);
-          if (e0 + j < valid && (u >> 20) == b) {
-            sm.cidx[pos] = e0 + j;
-            sm.ckey[pos] = u;
-            ++pos;
-          }
-        }
-      }
-      n_cand += tot;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) cur[j] = nxt[j];
-    }
-  }
-  __syncthreads();
-
-  // ---- resolve T among the candidates (all in bin b); add the chosen ones to the bitmap
-  uint32_t T, kk_eq, n_eq;
-  select_kth(sm, n_cand, kk, 1, b << 20, 0xFFF00000u, T, kk_eq, n_eq);
-  {
-    int tie_seen = 0;
-    for (int i0 = 0; i0 < n_cand; i0 += kThreads) {
-      const int i = i0 + tid;
-      const uint32_t u = i < n_cand ? sm.ckey[i] : 0u;
-      const bool gt = i < n_cand && u > T;
-      const bool eq = i < n_cand && u == T;
-      int tot;
-      const int rank = tie_seen + block_excl_scan(eq ? 1 : 0, sm.wsum, tot);
-      if (gt || (eq && rank < (int)kk_eq)) {
-        const int t = sm.cidx[i];
-        atomicOr(&sm.bits[t >> 5], 1u << (t & 31));
-      }
-      tie_seen += tot;
-    }
-  }
-  __syncthreads();
-  write_bitmap(sm, nwords, k, out);
-}
-
-__global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
+__global__ __launch_bounds__(kThreads, 4) void topk_kernel(TopkArgs a) {
   __shared__ TopkSmem sm;
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
@@ -461,11 +396,21 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     return;
   }
   const bool vec = ((reinterpret_cast<uintptr_t>(sc) & 15u) == 0);
+  float cur[kPer];
   if (valid >= kOneReadMin && k <= kCand / 4) {
-    if (topk_one_read(sm, sc, valid, k, out, vec)) return;
+    load16v(vec, sc, kPer * tid, valid, cur);          // in flight while the sample is processed
+    const uint32_t tau = sampled_tau(sm, sc, valid, k, vec);
+    if (select_from(sm, sc, valid, k, out, vec, tau, cur)) return;
     __syncthreads();
   }
-  topk_two_reads(sm, sc, valid, k, out, vec);
+  uint32_t tau;
+  if (exact_tau(sm, sc, valid, k, vec, tau)) {
+    __syncthreads();
+    load16v(vec, sc, kPer * tid, valid, cur);
+    if (select_from(sm, sc, valid, k, out, vec, tau, cur)) return;   // always: n >= k, n <= kCand
+  }
+  __syncthreads();
+  topk_radix_row(sm, sc, valid, k, out);
 }
 
 }  // namespace

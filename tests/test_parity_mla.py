@@ -121,9 +121,9 @@ def test_topk_hook_long_and_clustered_rows(pa_lib):
 
 
 def _sample_runs(valid):
-    """Where the top-k kernel's one-read path samples a row: 16 runs of 256 scores, run w
-    starting at w * (valid - 256) // 15 rounded down to a multiple of 4."""
-    return [((w * (valid - 256)) // 15) & ~3 for w in range(16)]
+    """Where the top-k kernel samples a row for its threshold: 8 runs of 512 scores, run w
+    starting at w * (valid - 512) // 7 rounded down to a multiple of 4."""
+    return [((w * (valid - 512)) // 7) & ~3 for w in range(8)]
 
 
 def test_topk_hook_one_read_and_its_fallbacks(pa_lib):
@@ -138,11 +138,11 @@ def test_topk_hook_one_read_and_its_fallbacks(pa_lib):
     rows.append(rng.standard_normal(n))                                   # plain
     r = rng.standard_normal(n)                                            # runs high: too few
     for a in _sample_runs(n):
-        r[a:a + 256] = 10.0 + rng.standard_normal(256)
+        r[a:a + 512] = 10.0 + rng.standard_normal(512)
     rows.append(r)
     r = 10.0 + rng.standard_normal(n)                                     # runs low: too many
     for a in _sample_runs(n):
-        r[a:a + 256] = rng.standard_normal(256)
+        r[a:a + 512] = rng.standard_normal(512)
     rows.append(r)
     r = rng.standard_normal(n)                                            # 2,000 ties, 1,548 taken
     pos = rng.permutation(n)
