@@ -149,11 +149,10 @@ __device__ void topk_radix_row(TopkSmem& sm, const float* sc, int valid, int k, 
       if ((u & mask) == prefix) atomicAdd(&sm.hist[(u >> shift) & 255u], 1u);
     }
     __syncthreads();
-    find_bin_from_top(sm, 256, kk);
+    find_bin_from_top(sm, 256, kk);           // its last barrier follows every histogram read
     prefix |= sm.sh_bin << shift;
     kk = sm.sh_kk;
     mask |= 0xFFu << shift;
-    __syncthreads();
   }
   const uint32_t T = prefix;
   int eq_seen = 0, written = 0;
@@ -303,12 +302,13 @@ __device__ bool select_from(TopkSmem& sm, const float* sc, int valid, int k, int
         if ((u & mask) == prefix) atomicAdd(&sm.hist[(u >> sh) & (nb - 1)], 1u);
       }
       __syncthreads();
+      // find_bin_from_top ends with a barrier after every histogram read, and the next pass
+      // rewrites sm.sh_* only after further barriers, so no barrier is needed here
       find_bin_from_top(sm, nb, kk);
       prefix |= sm.sh_bin << sh;
       kk = sm.sh_kk;
       n_eq = sm.sh_n;
       mask |= (uint32_t)(nb - 1) << sh;
-      __syncthreads();
     }
   }
   const uint32_t T = prefix, kk_eq = kk;
