@@ -111,16 +111,17 @@ struct TopkSmem {
   int n_cand;
 };
 
-// Bin d of sm.hist[0..nbins) (nbins a multiple of 4, at most 4 * kThreads) with G keys in
+// Bin d of hist[0..nbins) (sm.hist unless given; nbins a multiple of 4, at most 4 * kThreads) with G keys in
 // the bins above it and G < kk <= G + hist[d]: d -> sm.sh_bin, kk - G -> sm.sh_kk,
 // hist[d] -> sm.sh_n.  Each thread sums a group of 4 bins; a block scan in reversed
 // group order gives the count above every group.  The caller guarantees kk <= the total.
-__device__ void find_bin_from_top(TopkSmem& sm, int nbins, uint32_t kk) {
+__device__ void find_bin_from_top(TopkSmem& sm, int nbins, uint32_t kk, const uint32_t* hist = nullptr) {
+  if (hist == nullptr) hist = sm.hist;
   const int g = nbins / 4 - 1 - (int)threadIdx.x;
   uint32_t c[4] = {0u, 0u, 0u, 0u};
   if (g >= 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = sm.hist[4 * g + i];
+    for (int i = 0; i < 4; ++i) c[i] = hist[4 * g + i];
   }
   int tot;
   int above = block_excl_scan((int)(c[0] + c[1] + c[2] + c[3]), sm.wsum, tot);
@@ -192,7 +193,12 @@ __device__ uint32_t sampled_tau(TopkSmem& sm, const float* sc, int valid, int k,
       for (int i = 0; i < 4; ++i) skey[4 * hh + i] = score_key(sc[e + i]);
     }
   }
+  // first level in sm.hist, second level in the (still unused) candidate array; both and the
+  // candidate count are cleared under one barrier
+  uint32_t* hist2 = sm.cidx;
   for (int j = tid; j < kBins; j += kThreads) sm.hist[j] = 0u;
+  for (int j = tid; j < 512; j += kThreads) hist2[j] = 0u;
+  if (tid == 0) sm.n_cand = 0;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 8; ++i) atomicAdd(&sm.hist[skey[i] >> 21], 1u);
@@ -203,13 +209,11 @@ __device__ uint32_t sampled_tau(TopkSmem& sm, const float* sc, int valid, int k,
   const uint32_t rank = (uint32_t)min(kSample, max(kMinRank, want));
   find_bin_from_top(sm, kBins, rank);
   const uint32_t b11 = sm.sh_bin, rr = sm.sh_kk;
-  for (int j = tid; j < 512; j += kThreads) sm.hist[j] = 0u;
-  __syncthreads();
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    if ((skey[i] >> 21) == b11) atomicAdd(&sm.hist[(skey[i] >> 12) & 511u], 1u);
+    if ((skey[i] >> 21) == b11) atomicAdd(&hist2[(skey[i] >> 12) & 511u], 1u);
   __syncthreads();
-  find_bin_from_top(sm, 512, rr);
+  find_bin_from_top(sm, 512, rr, hist2);
   return (b11 << 21) | (sm.sh_bin << 12);
 }
 
@@ -220,6 +224,7 @@ __device__ bool exact_tau(TopkSmem& sm, const float* sc, int valid, int k, bool 
   const int tid = threadIdx.x;
   const int n_super = (valid + kSuper - 1) / kSuper;
   for (int j = tid; j < kBins; j += kThreads) sm.hist[j] = 0u;
+  if (tid == 0) sm.n_cand = 0;
   __syncthreads();
   float cur[kPer], nxt[kPer];
   load16v(vec, sc, kPer * tid, valid, cur);
@@ -240,16 +245,14 @@ __device__ bool exact_tau(TopkSmem& sm, const float* sc, int valid, int k, bool 
   return above_and_bin <= kCand;
 }
 
-// Steps 2 and 3 of the file comment for a threshold tau.  cur holds the first step's
-// scores (loads issued by the caller).  Returns false, uniformly over the workgroup and with
+// Steps 2 and 3 of the file comment for a threshold tau (sampled_tau or exact_tau, which
+// also clear sm.n_cand).  cur holds the first step's scores (loads issued by the caller).  Returns false, uniformly over the workgroup and with
 // nothing written to out, when fewer than k or more than kCand keys reached tau.
 __device__ bool select_from(TopkSmem& sm, const float* sc, int valid, int k, int32_t* out, bool vec, uint32_t tau,
                             float (&cur)[kPer]) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int n_super = (valid + kSuper - 1) / kSuper;
-  if (tid == 0) sm.n_cand = 0;
-  __syncthreads();
-  float nxt[kPer];
+  float nxt[kPer];                                     // sm.n_cand was cleared with tau's histogram
   for (int sI = 0; sI < n_super; ++sI) {
     const int e0 = sI * kSuper + kPer * tid;
     if (sI + 1 < n_super) load16v(vec, sc, e0 + kSuper, valid, nxt);
