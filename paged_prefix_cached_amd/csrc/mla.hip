@@ -236,12 +236,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     return pb >= 0 ? pb * kBs + idx % kBs : -1;
   };
   if constexpr (SPARSE) {
-    if constexpr (STAGED)
-      for (int j = tid; j < n_keys; j += NT) {
-        const uint32_t r = (uint32_t)sel_row(sel_g[j]) & kNoRow;   // -1 -> kNoRow
-        sel_lo[j] = (uint16_t)r;
-        sel_hi[j] = (uint8_t)(r >> 16);
+    if constexpr (STAGED) {
+      // all of a thread's selections, then all their table entries (at clamped, in-bounds
+      // columns), are loaded before any is resolved: two round trips rather than two per
+      // selection
+      constexpr int kPerT = (kSelLds + NT - 1) / NT;
+      int sel[kPerT], ent[kPerT];
+#pragma unroll
+      for (int u = 0; u < kPerT; ++u) {
+        const int j = tid + u * NT;
+        sel[u] = j < n_keys ? sel_g[j] : -1;
       }
+      if (n_lblocks > 0) {
+#pragma unroll
+        for (int u = 0; u < kPerT; ++u) ent[u] = bt_row[min(max(sel[u], 0) / kBs, n_lblocks - 1)];
+      } else {
+#pragma unroll
+        for (int u = 0; u < kPerT; ++u) ent[u] = -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kPerT; ++u) {
+        const int j = tid + u * NT;
+        const int idx = sel[u], pb = ent[u];
+        const bool ok = idx >= 0 && idx / kBs < n_lblocks && pb >= 0 && pb < num_blocks;
+        const uint32_t r = ok ? (uint32_t)(pb * kBs + idx % kBs) : kNoRow;
+        if (j < n_keys) {
+          sel_lo[j] = (uint16_t)r;
+          sel_hi[j] = (uint8_t)(r >> 16);
+        }
+      }
+    }
   } else {
     for (int j = tid; j < n_bt; j += NT) bt_s[j] = phys_block(bt_row, lb_base + j, n_lblocks, num_blocks);
   }
