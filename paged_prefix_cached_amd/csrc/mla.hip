@@ -75,10 +75,6 @@ __device__ __forceinline__ u32x4 fp8x8_to_f16x8(u32x2 b) {
 
 typedef __attribute__((address_space(3))) const uint8_t lds_u8;
 
-__device__ __forceinline__ u32x2 lds_read_b64(lds_u8* base, int off) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(base + off);
-}
-
 __device__ __forceinline__ u32x4 lds_read_b128(lds_u8* base, int off) {
   return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(base + off);
 }
